@@ -1,0 +1,187 @@
+/*
+ * ozaki2.h -- C ABI of libozaki2.so: FP64 matrix products emulated with
+ * Ozaki Scheme II on INT8 matrix cores of AMD Instinct MI355X (gfx950).
+ *
+ * Pages this interface follows:
+ *   [Q] "8ビットの整数で53ビットの倍精度を組み立てる。中国剰余定理をGPUに載せた
+ *       Ozaki Scheme II" (Qiita article), section "Ozaki Scheme IIのGPU実装"
+ *       and its subsections for steps 1-5;
+ *   [G] "Improved Scaling for Fast Mode of Ozaki Scheme II" (technical
+ *       summary), section Methodik (the proposed fast-mode scaling) and
+ *       section Problemstellung (fast and accurate modes).
+ *
+ * The pages give no programming interface; this one follows BLAS DGEMM
+ * conventions: C := A * B (alpha = 1, beta = 0), column-major storage, no
+ * transposes.
+ *
+ * Arguments common to the product entry points
+ *   m, n, k   sizes: A is m x k, B is k x n, C is m x n; each >= 0.
+ *   A, lda    DEVICE pointer to A, column-major, element (i, h) at
+ *             A[i + h*lda]; lda >= max(1, m).
+ *   B, ldb    DEVICE pointer to B, element (h, j) at B[h + j*ldb];
+ *             ldb >= max(1, k).
+ *   C, ldc    DEVICE pointer to C, element (i, j) at C[i + j*ldc];
+ *             ldc >= max(1, m). C must not overlap A, B or the workspace.
+ *   num_moduli N in [2, 20]: the first N moduli of the implementation's
+ *             table (256, 255, 253, 251, 247, 241, 239, 233, 229, 227, 223,
+ *             217, 211, 199, 197, 193, 191, 181, 179, 173), the largest
+ *             pairwise-coprime integers <= 256 ([Q] section
+ *             256以下の法の選び方(手順2) and its footnote). N >= 14 reaches
+ *             the accuracy of native FP64 on typical inputs
+ *             ([Q] section 行列積の回数と性能).
+ *   mode      OZAKI2_FAST: the scale-invariant Cauchy-Schwarz scaling of [G]
+ *             section Methodik; OZAKI2_ACCURATE: one extra INT8 GEMM bounds
+ *             the products before scaling ([Q] section
+ *             2の累乗による整数化(手順1と5), [G] section Problemstellung).
+ *   stream    hipStream_t to enqueue on (NULL = default stream). All device
+ *             work is asynchronous; no call synchronises the stream.
+ *
+ * Memory ownership: A, B, C and any workspace belong to the caller. The
+ * library keeps one cached workspace per device for ozaki2_dgemm (freed by
+ * ozaki2_finalize) and small per-device constant tables.
+ *
+ * Status codes: 0 success; -i the i-th argument (1-based, in signature order)
+ * is invalid, as in BLAS xerbla; positive codes are the OZAKI2_ERR_* values.
+ * All argument checks happen before any HIP call, so a negative status
+ * never touches the device.
+ *
+ * Values: inputs should be finite. A row of A (or column of B) holding Inf
+ * or NaN turns the matching row (column) of C into NaN. Zero rows and
+ * columns give exact zeros. Results are bitwise reproducible from run to run
+ * and equal, for every input whose rows and columns are finite,
+ * RN(sum_h trunc(2^e_i a_ih) trunc(2^f_j b_hj)) * 2^-(e_i + f_j) with the
+ * exponents e, f the chosen mode computes.
+ */
+#ifndef OZAKI2_H
+#define OZAKI2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ozaki2_mode {
+    OZAKI2_FAST = 0,     /* proposed scale-invariant fast-mode scaling ([G] Methodik) */
+    OZAKI2_ACCURATE = 1  /* extra INT8 bound GEMM ([G] Problemstellung, mode 1) */
+};
+
+enum ozaki2_status {
+    OZAKI2_SUCCESS = 0,
+    OZAKI2_ERR_HIP = 1,         /* a HIP runtime call or kernel launch failed */
+    OZAKI2_ERR_WORKSPACE = 2,   /* workspace too small, or its allocation failed */
+    OZAKI2_ERR_UNSUPPORTED = 3  /* k >= 2^17: int32 sums would no longer be exact
+                                   ([Q] section 誤差のないINT8行列積(手順3)) */
+};
+
+#define OZAKI2_MAX_MODULI 20
+#define OZAKI2_MAX_K 131071 /* 2^17 - 1 */
+
+/*
+ * C := A * B emulated by Ozaki Scheme II ([Q] steps 1-5). Uses a workspace
+ * cached per device, grown on first use of a larger problem (that growth is
+ * the only blocking action: hipMalloc after synchronising the device).
+ * Calls on one device are serialised by a mutex; use ozaki2_dgemm_ws for
+ * concurrent streams.
+ * Returns 0, -1..-11 for an invalid argument (m, n, k, A, lda, B, ldb, C,
+ * ldc, num_moduli, mode), OZAKI2_ERR_UNSUPPORTED, OZAKI2_ERR_WORKSPACE or
+ * OZAKI2_ERR_HIP. m == 0 or n == 0 returns at once; k == 0 fills C with zeros.
+ */
+int ozaki2_dgemm(int64_t m, int64_t n, int64_t k,
+                 const double *A, int64_t lda, const double *B, int64_t ldb,
+                 double *C, int64_t ldc, int num_moduli, int mode, void *stream);
+
+/*
+ * Bytes of device workspace ozaki2_dgemm_ws needs for this problem
+ * (0 for invalid arguments or empty products). Host-only; no HIP call.
+ */
+size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
+
+/*
+ * As ozaki2_dgemm, with a caller-provided DEVICE workspace of at least
+ * ozaki2_workspace_size(...) bytes, 256-byte aligned. Never allocates and is
+ * re-entrant; calls that share one workspace must be ordered on one stream.
+ * Returns as ozaki2_dgemm; -12 if workspace is NULL (while needed),
+ * OZAKI2_ERR_WORKSPACE if workspace_bytes is too small.
+ */
+int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k,
+                    const double *A, int64_t lda, const double *B, int64_t ldb,
+                    double *C, int64_t ldc, int num_moduli, int mode,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test entry point (layout of the copies is stable, timing is not): runs
+ * ozaki2_dgemm_ws and also copies intermediates into caller DEVICE buffers,
+ * each of which may be NULL to skip it:
+ *   e_out    int32 [m]: exponent of each row of A (mu_i = 2^e_i), step 1;
+ *   f_out    int32 [n]: exponent of each column of B;
+ *            INT32_MIN marks a row/column holding Inf or NaN;
+ *   resA_out int8 [N][m][k]: residues of trunc(2^e_i a_ih) mod p_l in the
+ *            symmetric range (-(p-1)/2..(p-1)/2, -128..127 for 256), step 2;
+ *   resB_out int8 [N][n][k]: residues of trunc(2^f_j b_hj), element
+ *            (l, j, h) at resB_out[(l*n + j)*k + h];
+ *   prod_out int32 [N][n][m]: exact residue products
+ *            Q_l(i, j) = sum_h resA(l,i,h) resB(l,j,h) at prod_out[(l*n + j)*m + i], step 3;
+ *   red_out  uint8 [N][n][m]: Q_l mod p_l in [0, p_l), same indexing.
+ * Argument errors as ozaki2_dgemm_ws (workspace_bytes must also cover
+ * ozaki2_debug_workspace_size); -13..-18 for a NULL-but-needed debug buffer
+ * is never returned (NULL means skip).
+ */
+int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k,
+                       const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode,
+                       void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
+                       int32_t *prod_out, uint8_t *red_out, void *stream);
+
+/* Workspace bytes for ozaki2_dgemm_debug (larger: raw int32 products). */
+size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
+
+/* Largest supported number of moduli (20). */
+int ozaki2_max_moduli(void);
+
+/*
+ * Writes the first num_moduli moduli into the HOST array out[num_moduli].
+ * Returns 0, or -1 if num_moduli is outside [1, 20], -2 if out is NULL.
+ */
+int ozaki2_moduli(int num_moduli, int32_t *out);
+
+/*
+ * Writes to HOST *out the constant P'_prop of [G] section Methodik for N
+ * moduli: 0.5 * log2((P - 1) / 2) rounded down to a double, P the product of
+ * the moduli. Returns 0, -1 for N outside [2, 20], -2 for out NULL.
+ */
+int ozaki2_scaling_constant(int num_moduli, double *out);
+
+/*
+ * Writes the CRT weight W_l = (P/p_l) * ((P/p_l)^-1 mod p_l) ([Q] section
+ * 秦九韶の大衍求一術, the 用数) of modulus l for N moduli into the HOST array
+ * out_le32 as little-endian 32-bit limbs (out_limbs entries). Returns the
+ * number of limbs used, or a negative argument index.
+ */
+int ozaki2_crt_weight(int num_moduli, int l, uint32_t *out_le32, int out_limbs);
+
+/* Static text for a status code. */
+const char *ozaki2_status_string(int status);
+
+/*
+ * Per-phase timing with HIP events recorded on the caller's stream around
+ * each phase of every product call (phases: 0 scaling/exponents, 1 residue
+ * split, 2 INT8 GEMMs, 3 CRT + unscale). ozaki2_timing_enable(max_calls)
+ * creates the events (0 turns timing off); ozaki2_timing_read synchronises
+ * the recorded events, writes the summed milliseconds per phase to
+ * HOST ms_out[4] and the number of timed calls to *calls, and clears the
+ * record. Returns 0 or OZAKI2_ERR_HIP.
+ */
+int ozaki2_timing_enable(int max_calls);
+int ozaki2_timing_read(double *ms_out, int *calls);
+
+/* Frees the cached workspaces, timing events and tables. */
+void ozaki2_finalize(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OZAKI2_H */

@@ -1,0 +1,190 @@
+"""Python binding of libozaki2: FP64 matrix products emulated by Ozaki Scheme II
+on the INT8 matrix cores of MI355X (gfx950).
+
+Argument marshalling only: every step of the product runs in the HIP kernels
+of ``libozaki2.so`` (built in-tree by ``python -m rns_emulated_fp64_amd.build``).
+There is no CPU fallback; loading fails loudly when the library is missing.
+
+Functions named like the C ABI (``ozaki2_dgemm`` ...) take plain integers and
+device pointers exactly as ``include/ozaki2.h`` documents. ``dgemm`` is the
+convenience form on torch tensors (torch provides device memory and streams).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libozaki2.so")
+
+FAST = 0
+ACCURATE = 1
+MODES = {"fast": FAST, "accurate": ACCURATE}
+PHASES = ("scale", "split", "gemm", "crt")
+
+#: every symbol include/ozaki2.h declares
+EXPORTS = (
+    "ozaki2_dgemm", "ozaki2_workspace_size", "ozaki2_dgemm_ws", "ozaki2_dgemm_debug",
+    "ozaki2_debug_workspace_size", "ozaki2_max_moduli", "ozaki2_moduli", "ozaki2_scaling_constant",
+    "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
+    "ozaki2_finalize",
+)
+
+_lib = None
+
+
+class Ozaki2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libozaki2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rns_emulated_fp64_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    prod = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32]
+    L.ozaki2_dgemm.argtypes = prod + [p]
+    L.ozaki2_dgemm.restype = i32
+    L.ozaki2_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.ozaki2_workspace_size.restype = sz
+    L.ozaki2_debug_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.ozaki2_debug_workspace_size.restype = sz
+    L.ozaki2_dgemm_ws.argtypes = prod + [p, sz, p]
+    L.ozaki2_dgemm_ws.restype = i32
+    L.ozaki2_dgemm_debug.argtypes = prod + [p, sz, p, p, p, p, p, p, p]
+    L.ozaki2_dgemm_debug.restype = i32
+    L.ozaki2_max_moduli.argtypes = []
+    L.ozaki2_max_moduli.restype = i32
+    L.ozaki2_moduli.argtypes = [i32, p]
+    L.ozaki2_moduli.restype = i32
+    L.ozaki2_scaling_constant.argtypes = [i32, p]
+    L.ozaki2_scaling_constant.restype = i32
+    L.ozaki2_crt_weight.argtypes = [i32, i32, p, i32]
+    L.ozaki2_crt_weight.restype = i32
+    L.ozaki2_status_string.argtypes = [i32]
+    L.ozaki2_status_string.restype = ctypes.c_char_p
+    L.ozaki2_timing_enable.argtypes = [i32]
+    L.ozaki2_timing_enable.restype = i32
+    L.ozaki2_timing_read.argtypes = [p, p]
+    L.ozaki2_timing_read.restype = i32
+    L.ozaki2_finalize.argtypes = []
+    L.ozaki2_finalize.restype = None
+    _lib = L
+    return L
+
+
+# ---- same names as the C ABI: plain integers / device pointers ----------------
+def ozaki2_dgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) -> int:
+    return lib().ozaki2_dgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_workspace_size(m, n, k, num_moduli, mode) -> int:
+    return lib().ozaki2_workspace_size(m, n, k, num_moduli, mode)
+
+
+def ozaki2_debug_workspace_size(m, n, k, num_moduli, mode) -> int:
+    return lib().ozaki2_debug_workspace_size(m, n, k, num_moduli, mode)
+
+
+def ozaki2_dgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_dgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace,
+                                 workspace_bytes, stream)
+
+
+def ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                       e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
+    return lib().ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace,
+                                    workspace_bytes, e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_max_moduli() -> int:
+    return lib().ozaki2_max_moduli()
+
+
+def ozaki2_moduli(num_moduli: int) -> list[int]:
+    out = (ctypes.c_int32 * max(num_moduli, 1))()
+    st = lib().ozaki2_moduli(num_moduli, out)
+    if st:
+        raise Ozaki2Error(st, "ozaki2_moduli")
+    return list(out)[:num_moduli]
+
+
+def ozaki2_scaling_constant(num_moduli: int) -> float:
+    out = ctypes.c_double()
+    st = lib().ozaki2_scaling_constant(num_moduli, ctypes.byref(out))
+    if st:
+        raise Ozaki2Error(st, "ozaki2_scaling_constant")
+    return out.value
+
+
+def ozaki2_crt_weight(num_moduli: int, l: int) -> int:
+    limbs = (ctypes.c_uint32 * 8)()
+    used = lib().ozaki2_crt_weight(num_moduli, l, limbs, 8)
+    if used < 0:
+        raise Ozaki2Error(used, "ozaki2_crt_weight")
+    return sum(int(limbs[i]) << (32 * i) for i in range(used))
+
+
+def status_string(status: int) -> str:
+    return lib().ozaki2_status_string(status).decode()
+
+
+def ozaki2_timing_enable(max_calls: int) -> None:
+    st = lib().ozaki2_timing_enable(max_calls)
+    if st:
+        raise Ozaki2Error(st, "ozaki2_timing_enable")
+
+
+def ozaki2_timing_read() -> tuple[dict, int]:
+    ms = (ctypes.c_double * 4)()
+    calls = ctypes.c_int()
+    st = lib().ozaki2_timing_read(ms, ctypes.byref(calls))
+    if st:
+        raise Ozaki2Error(st, "ozaki2_timing_read")
+    return dict(zip(PHASES, list(ms))), calls.value
+
+
+def ozaki2_finalize() -> None:
+    lib().ozaki2_finalize()
+
+
+# ---- torch convenience -------------------------------------------------------
+def _mode(mode) -> int:
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def dgemm(A, B, num_moduli: int = 16, mode="fast", out=None, workspace=None):
+    """C = A @ B for float64 CUDA (HIP) tensors in row-major layout.
+
+    Row-major C = A B is column-major C^T = B^T A^T, so the library is called
+    with the operands swapped; the scaling is symmetric in the two operands.
+    """
+    import torch
+
+    if A.dtype != torch.float64 or B.dtype != torch.float64 or not A.is_cuda or not B.is_cuda:
+        raise TypeError("A and B must be float64 tensors on the GPU")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError("shapes do not multiply")
+    A = A.contiguous()
+    B = B.contiguous()
+    m, k = A.shape
+    n = B.shape[1]
+    C = out if out is not None else torch.empty((m, n), dtype=torch.float64, device=A.device)
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    md = _mode(mode)
+    if workspace is None:
+        st = ozaki2_dgemm(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                          num_moduli, md, stream)
+    else:
+        st = ozaki2_dgemm_ws(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                             num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             stream)
+    if st:
+        raise Ozaki2Error(st, "ozaki2_dgemm")
+    return C

@@ -1,0 +1,371 @@
+// api.cpp -- the C ABI of libozaki2 (declared in include/ozaki2.h): argument
+// checks, workspace layout, the order of the phases, per-phase timing.
+//
+// [Q] = Qiita article "8ビットの整数で53ビットの倍精度を組み立てる。中国剰余定理を
+// GPUに載せたOzaki Scheme II"; [G] = "Improved Scaling for Fast Mode of Ozaki
+// Scheme II". The phases run in the article's order: powers of two (step 1),
+// residues (step 2), one INT8 product per modulus (step 3), reconstruction
+// and unscaling (steps 4 and 5); [G] section Methodik gives the fast-mode
+// exponents and section Problemstellung the two modes.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "ozaki2.h"
+#include "tables.h"
+
+namespace oz2 {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
+
+// Checks in signature order; returns 0 or -(index of the first bad argument).
+int validate(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+             const double *C, int64_t ldc, int nmod, int mode) {
+    if (m < 0) return -1;
+    if (n < 0) return -2;
+    if (k < 0) return -3;
+    if (A == nullptr && m > 0 && k > 0) return -4;
+    if (lda < (m > 1 ? m : 1)) return -5;
+    if (B == nullptr && k > 0 && n > 0) return -6;
+    if (ldb < (k > 1 ? k : 1)) return -7;
+    if (C == nullptr && m > 0 && n > 0) return -8;
+    if (ldc < (m > 1 ? m : 1)) return -9;
+    if (nmod < 2 || nmod > kMaxModuli) return -10;
+    if (mode != OZAKI2_FAST && mode != OZAKI2_ACCURATE) return -11;
+    return 0;
+}
+
+// Sizes are limited so that every offset below fits comfortably in 63 bits.
+bool layout_fits(int64_t m, int64_t n, int64_t k) {
+    const int64_t lim = (int64_t)1 << 31;
+    return m < lim && n < lim && k <= OZAKI2_MAX_K;
+}
+
+Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool debug) {
+    Layout L{};
+    L.m_pad = round_up(m > 0 ? m : 1, kTileM);
+    L.n_pad = round_up(n > 0 ? n : 1, kTileN);
+    L.k_pad = round_up(k > 0 ? k : 1, kKPad);
+    L.kb = L.k_pad / 32;
+    // k-chunks of the row-norm pass: enough blocks to fill 256 CUs several times
+    const int64_t rowblocks = (m + 255) / 256 > 0 ? (m + 255) / 256 : 1;
+    int64_t want = (2048 + rowblocks - 1) / rowblocks;
+    int64_t maxc = (k + 15) / 16 > 0 ? (k + 15) / 16 : 1;
+    if (want > maxc) want = maxc;
+    if (want > 65535) want = 65535;
+    if (want < 1) want = 1;
+    L.kchunk = (k + want - 1) / want > 0 ? (k + want - 1) / want : 1;
+    L.nchunks = (int)((k + L.kchunk - 1) / L.kchunk > 0 ? (k + L.kchunk - 1) / L.kchunk : 1);
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    const size_t mp = (size_t)L.m_pad, np = (size_t)L.n_pad, kp = (size_t)L.k_pad, mm = (size_t)(m > 0 ? m : 1);
+    L.e = take(4 * mp);
+    L.f = take(4 * np);
+    L.ga = take(4 * mp);
+    L.gb = take(4 * np);
+    L.part_s = take(8 * (size_t)L.nchunks * mm);
+    L.part_g = take(4 * (size_t)L.nchunks * mm);
+    L.part_bad = take(4 * (size_t)L.nchunks * mm);
+    if (mode == OZAKI2_ACCURATE) {
+        L.rowmax = take(4 * mp);
+        L.colmax = take(4 * np);
+        L.abar = take(mp * kp);
+        L.bbar = take(np * kp);
+    }
+    L.ra = take((size_t)nmod * mp * kp);
+    L.rb = take((size_t)nmod * np * kp);
+    L.planes = take((size_t)nmod * np * mp);
+    if (debug) L.raw = take(4 * (size_t)nmod * np * mp);
+    L.total = off;
+    return L;
+}
+
+// ---- timing ---------------------------------------------------------------
+struct Timing {
+    std::mutex mu;
+    std::vector<hipEvent_t> ev;  // (kNumPhases + 1) per call
+    int max_calls = 0;
+    int used = 0;
+};
+Timing g_timing;
+
+void timing_free_locked() {
+    for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
+    g_timing.ev.clear();
+    g_timing.max_calls = 0;
+    g_timing.used = 0;
+}
+
+// Event slots for one call, or nullptr when timing is off or full.
+hipEvent_t *timing_slots() {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.used >= g_timing.max_calls) return nullptr;
+    return &g_timing.ev[(size_t)(g_timing.used++) * (kNumPhases + 1)];
+}
+
+// ---- cached workspace per device ------------------------------------------
+struct Cache {
+    std::mutex mu;
+    std::vector<void *> ptr;
+    std::vector<size_t> bytes;
+};
+Cache g_cache;
+
+#define HIP_TRY(x)                               \
+    do {                                         \
+        if ((x) != hipSuccess) return OZAKI2_ERR_HIP; \
+    } while (0)
+
+struct DebugOut {
+    int32_t *e, *f;
+    int8_t *ra, *rb;
+    int32_t *prod;
+    uint8_t *red;
+};
+
+int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb, double *C,
+        int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
+    const Tables *T = get_tables(nmod);
+    hipEvent_t *ev = timing_slots();
+    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+
+    // Step 1: exponents ([G] Methodik for fast mode; accurate mode bounds the
+    // products with one extra INT8 GEMM first).
+    HIP_TRY(launch_row_norms(A, m, k, lda, L, ws, s));
+    HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
+    HIP_TRY(launch_col_exponents(B, k, n, ldb, T->Pp, L, ws, s));
+    if (mode == OZAKI2_ACCURATE) {
+        HIP_TRY(launch_quantize(A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
+                                L.m_pad, L, s));
+        HIP_TRY(launch_quantize(B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
+                                L.n_pad, L, s));
+        HIP_TRY(launch_fill_i32((int32_t *)(ws + L.rowmax), L.m_pad, 0, s));
+        HIP_TRY(launch_fill_i32((int32_t *)(ws + L.colmax), L.n_pad, 0, s));
+        HIP_TRY(launch_gemm_bound((const int8_t *)(ws + L.abar), (const int8_t *)(ws + L.bbar),
+                                  (int32_t *)(ws + L.rowmax), (int32_t *)(ws + L.colmax), L, s));
+        HIP_TRY(launch_accurate_exponents(m, n, T->Pp, L, ws, s));
+    }
+    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
+
+    // Steps 1 + 2: integerize and split into residues.
+    const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
+    HIP_TRY(launch_split(A, m, k, lda, false, e, T->split, (int8_t *)(ws + L.ra), L.m_pad, L, s));
+    HIP_TRY(launch_split(B, n, k, ldb, true, f, T->split, (int8_t *)(ws + L.rb), L.n_pad, L, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+
+    // Step 3: one exact INT8 product per modulus, reduced mod p_l.
+    HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, T->mod,
+                            (uint8_t *)(ws + L.planes), L, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+
+    // Steps 4 + 5: reconstruction and unscaling.
+    HIP_TRY(launch_crt((const uint8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s));
+    if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+
+    if (dbg) {
+        if (dbg->e) HIP_TRY(hipMemcpyAsync(dbg->e, e, 4 * (size_t)m, hipMemcpyDeviceToDevice, s));
+        if (dbg->f) HIP_TRY(hipMemcpyAsync(dbg->f, f, 4 * (size_t)n, hipMemcpyDeviceToDevice, s));
+        if (dbg->ra)
+            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.ra), nmod, m, k, L.m_pad, L, dbg->ra, s));
+        if (dbg->rb)
+            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.rb), nmod, n, k, L.n_pad, L, dbg->rb, s));
+        if (dbg->red)
+            HIP_TRY(launch_copy_planes_u8((const uint8_t *)(ws + L.planes), nmod, m, n, L, dbg->red, s));
+        if (dbg->prod) {
+            HIP_TRY(launch_gemm_raw((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod,
+                                    (int32_t *)(ws + L.raw), L, s));
+            HIP_TRY(launch_copy_planes_i32((const int32_t *)(ws + L.raw), nmod, m, n, L, dbg->prod, s));
+        }
+    }
+    return OZAKI2_SUCCESS;
+}
+
+// Common front end of the product entry points.
+int front(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb, double *C,
+          int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, bool use_cache, const DebugOut *dbg,
+          void *stream) {
+    int st = validate(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode);
+    if (st) return st;
+    if (!layout_fits(m, n, k)) return OZAKI2_ERR_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    if (m == 0 || n == 0) return OZAKI2_SUCCESS;
+    if (k == 0) {
+        HIP_TRY(launch_zero_fill(C, m, n, ldc, s));
+        return OZAKI2_SUCCESS;
+    }
+    const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr);
+    if (!use_cache) {
+        if (workspace == nullptr) return -12;
+        if (wbytes < L.total) return OZAKI2_ERR_WORKSPACE;
+        return run(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
+    }
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lk(g_cache.mu);
+    if ((int)g_cache.ptr.size() <= dev) {
+        g_cache.ptr.resize(dev + 1, nullptr);
+        g_cache.bytes.resize(dev + 1, 0);
+    }
+    if (g_cache.bytes[dev] < L.total) {
+        if (g_cache.ptr[dev]) {
+            HIP_TRY(hipDeviceSynchronize());
+            (void)hipFree(g_cache.ptr[dev]);
+            g_cache.ptr[dev] = nullptr;
+            g_cache.bytes[dev] = 0;
+        }
+        void *p = nullptr;
+        if (hipMalloc(&p, L.total) != hipSuccess) return OZAKI2_ERR_WORKSPACE;
+        g_cache.ptr[dev] = p;
+        g_cache.bytes[dev] = L.total;
+    }
+    return run(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
+}
+
+}  // namespace
+}  // namespace oz2
+
+using namespace oz2;
+
+extern "C" {
+
+int ozaki2_dgemm(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                 double *C, int64_t ldc, int num_moduli, int mode, void *stream) {
+    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
+}
+
+size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode) {
+    if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
+                 m > 1 ? m : 1, num_moduli, mode))
+        return 0;
+    if (!layout_fits(m, n, k) || m == 0 || n == 0 || k == 0) return 0;
+    return make_layout(m, n, k, num_moduli, mode, false).total;
+}
+
+size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode) {
+    if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
+                 m > 1 ? m : 1, num_moduli, mode))
+        return 0;
+    if (!layout_fits(m, n, k) || m == 0 || n == 0 || k == 0) return 0;
+    return make_layout(m, n, k, num_moduli, mode, true).total;
+}
+
+int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                    double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, nullptr,
+                 stream);
+}
+
+int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
+                       uint8_t *red_out, void *stream) {
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d, stream);
+}
+
+int ozaki2_max_moduli(void) { return kMaxModuli; }
+
+int ozaki2_moduli(int num_moduli, int32_t *out) {
+    if (num_moduli < 1 || num_moduli > kMaxModuli) return -1;
+    if (out == nullptr) return -2;
+    greedy_moduli(num_moduli, out);
+    return 0;
+}
+
+int ozaki2_scaling_constant(int num_moduli, double *out) {
+    if (num_moduli < 2 || num_moduli > kMaxModuli) return -1;
+    if (out == nullptr) return -2;
+    *out = get_tables(num_moduli)->Pp;
+    return 0;
+}
+
+int ozaki2_crt_weight(int num_moduli, int l, uint32_t *out_le32, int out_limbs) {
+    if (num_moduli < 2 || num_moduli > kMaxModuli) return -1;
+    if (l < 0 || l >= num_moduli) return -2;
+    if (out_le32 == nullptr) return -3;
+    const Tables *T = get_tables(num_moduli);
+    if (out_limbs < T->weight_limbs) return -4;
+    for (int i = 0; i < out_limbs; ++i) out_le32[i] = i < 8 ? T->weight[l][i] : 0u;
+    return T->weight_limbs;
+}
+
+const char *ozaki2_status_string(int status) {
+    switch (status) {
+    case OZAKI2_SUCCESS: return "success";
+    case OZAKI2_ERR_HIP: return "HIP runtime or kernel launch error";
+    case OZAKI2_ERR_WORKSPACE: return "workspace too small or allocation failed";
+    case OZAKI2_ERR_UNSUPPORTED: return "unsupported size (k must be below 2^17, m and n below 2^31)";
+    default: break;
+    }
+    if (status < 0) return "invalid argument (status is minus its 1-based position)";
+    return "unknown status";
+}
+
+int ozaki2_timing_enable(int max_calls) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    timing_free_locked();
+    if (max_calls <= 0) return OZAKI2_SUCCESS;
+    g_timing.ev.resize((size_t)max_calls * (kNumPhases + 1));
+    for (hipEvent_t &e : g_timing.ev) {
+        if (hipEventCreate(&e) != hipSuccess) {
+            e = nullptr;
+            return OZAKI2_ERR_HIP;
+        }
+    }
+    g_timing.max_calls = max_calls;
+    g_timing.used = 0;
+    return OZAKI2_SUCCESS;
+}
+
+int ozaki2_timing_read(double *ms_out, int *calls) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double acc[kNumPhases] = {0, 0, 0, 0};
+    for (int c = 0; c < g_timing.used; ++c) {
+        hipEvent_t *ev = &g_timing.ev[(size_t)c * (kNumPhases + 1)];
+        if (hipEventSynchronize(ev[kNumPhases]) != hipSuccess) return OZAKI2_ERR_HIP;
+        for (int p = 0; p < kNumPhases; ++p) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, ev[p], ev[p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
+            acc[p] += ms;
+        }
+    }
+    if (ms_out)
+        for (int p = 0; p < kNumPhases; ++p) ms_out[p] = acc[p];
+    if (calls) *calls = g_timing.used;
+    g_timing.used = 0;
+    return OZAKI2_SUCCESS;
+}
+
+void ozaki2_finalize(void) {
+    {
+        std::lock_guard<std::mutex> lk(g_cache.mu);
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        for (size_t d = 0; d < g_cache.ptr.size(); ++d) {
+            if (g_cache.ptr[d]) {
+                (void)hipSetDevice((int)d);
+                (void)hipDeviceSynchronize();
+                (void)hipFree(g_cache.ptr[d]);
+            }
+        }
+        (void)hipSetDevice(cur);
+        g_cache.ptr.clear();
+        g_cache.bytes.clear();
+    }
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    timing_free_locked();
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// common.h -- declarations shared by the host API (api.cpp) and the HIP
+// kernels (kernels.hip) of libozaki2.
+//
+// Ozaki Scheme II steps follow the Qiita article "8ビットの整数で53ビットの倍精度
+// を組み立てる。中国剰余定理をGPUに載せたOzaki Scheme II" ([Q]) and the summary
+// "Improved Scaling for Fast Mode of Ozaki Scheme II" ([G]).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace oz2 {
+
+constexpr int kMaxModuli = 20;
+constexpr int kChunks = 4;          // CRT weights and P in 40-bit pieces (4 x 40 >= 156 bits)
+constexpr int kChunkBits = 40;
+constexpr int kExpNonfinite = INT32_MIN;  // exponent marker: row/column holds Inf or NaN
+constexpr int kExpEmpty = -4000;          // max-exponent marker of an all-zero row/column
+
+// Tiling of the packed int8 operands and of the GEMM. A packed operand of R
+// rows and K columns (K a multiple of kKPad) is stored per modulus as
+// [R/32][K/32] fragment blocks of 1 KiB; inside a block, lane L (0..63) owns
+// 16 bytes at L*16 holding row (L % 32) and columns 16*(L / 32) .. +15. This is
+// the operand order of v_mfma_i32_32x32x32_i8, so every global->LDS and
+// LDS->register move is a contiguous 1 KiB per wavefront.
+constexpr int kTileM = 256;   // GEMM block tile rows (A side)
+constexpr int kTileN = 256;   // GEMM block tile columns (B side)
+constexpr int kKPad = 128;    // K padding granule (split kernel tile width)
+
+// Host-computed constants for the residue split ([Q] steps 1 and 2).
+struct SplitConsts {
+    int n;                      // number of moduli; moduli[0] is 256
+    double p[kMaxModuli];       // moduli as doubles
+    double pinv[kMaxModuli];    // RN(1 / p)
+    double c42[kMaxModuli];     // 2^42 mod p, symmetric range
+};
+
+// Host-computed constants for the CRT reconstruction ([Q] step 4).
+struct CrtConsts {
+    int n;
+    double w[kMaxModuli][kChunks];  // weight W_l = (P/p_l)((P/p_l)^-1 mod p_l), 40-bit pieces
+    double P[kChunks];              // P, 40-bit pieces
+    double H[kChunks];              // P / 2, 40-bit pieces
+    double pinv120;                 // RN(2^120 / P)
+};
+
+// Constants for the GEMM epilogue (reduction mod p_l).
+struct ModConsts {
+    double p[kMaxModuli];
+    double pinv[kMaxModuli];
+};
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct Layout {
+    int64_t m_pad, n_pad, k_pad, kb;  // kb = k_pad / 32
+    int nchunks;                      // k-chunks of the row-norm pass over A
+    int64_t kchunk;
+    size_t e, f, ga, gb;              // int32 [m_pad], [n_pad], [m_pad], [n_pad]
+    size_t part_s, part_g, part_bad;  // row-norm partials [nchunks][m]
+    size_t rowmax, colmax;            // int32 [m_pad], [n_pad] (accurate mode)
+    size_t abar, bbar;                // int8 packed bound operands (accurate mode)
+    size_t ra, rb;                    // int8 packed residues [N][m_pad][k_pad], [N][n_pad][k_pad]
+    size_t planes;                    // uint8 [N][n_pad][m_pad]: products mod p
+    size_t raw;                       // int32 [N][n_pad][m_pad] (debug only)
+    size_t total;
+};
+
+enum Phase { kPhaseScale = 0, kPhaseSplit = 1, kPhaseGemm = 2, kPhaseCrt = 3, kNumPhases = 4 };
+
+// ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
+hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L,
+                            char *ws, hipStream_t s);
+hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s);
+hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp,
+                                const Layout &L, char *ws, hipStream_t s);
+hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                        const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad,
+                        const Layout &L, hipStream_t s);
+hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
+                           hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
+hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc,
+                           uint8_t *planes, const Layout &L, hipStream_t s);
+hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw,
+                           const Layout &L, hipStream_t s);
+hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
+                             const Layout &L, hipStream_t s);
+hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws,
+                                     hipStream_t s);
+hipError_t launch_crt(const uint8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s);
+hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
+hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
+                                  int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
+hipError_t launch_copy_planes_u8(const uint8_t *planes, int nmod, int64_t m, int64_t n, const Layout &L,
+                                 uint8_t *out, hipStream_t s);
+hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
+                                  int32_t *out, hipStream_t s);
+
+}  // namespace oz2

@@ -1,0 +1,873 @@
+// kernels.hip -- gfx950 (MI355X) kernels of the Ozaki Scheme II FP64 GEMM
+// emulation.
+//
+// Pages: [Q] Qiita article "8ビットの整数で53ビットの倍精度を組み立てる。中国剰余
+// 定理をGPUに載せたOzaki Scheme II", section "Ozaki Scheme IIのGPU実装" (steps 1-5);
+// [G] "Improved Scaling for Fast Mode of Ozaki Scheme II", section Methodik.
+//
+// Phases and the bound each one lives under:
+//   norms + exponents  (step 1, [G] Methodik)          HBM: reads A and B once
+//   residue split      (steps 1 + 2)                    HBM / FP64 VALU
+//   INT8 GEMMs         (step 3), one per modulus        INT8 MFMA
+//   CRT + unscale      (steps 4 + 5)                    HBM / FP64 VALU
+//
+// Compiled with -ffp-contract=off: every product and sum below rounds on its
+// own unless an fma() is written out, which the exact integer arithmetic
+// relies on.
+#include <float.h>
+#include <math.h>
+
+#include "common.h"
+
+namespace oz2 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr double kU32 = 0x1p-24;  // unit roundoff of binary32; [G] uses a 4 u32 margin
+
+// ---------------------------------------------------------------------------
+// Step 1: squared norms with an exact power-of-two rescale
+// ---------------------------------------------------------------------------
+// A running pair (s, g) stands for s * 4^g: the sum of squares of the entries
+// scaled by 2^-g, where 2^g is the smallest power of two above the largest
+// |entry| seen so far. Rescaling by powers of two is exact, so the result is
+// the sum of (a * 2^-G)^2 for the final G whatever the order of the maxima,
+// it cannot overflow or underflow, and a row scaled by 2^s gives the same s
+// bit for bit with G shifted by s (the scale invariance of [G] Methodik 2).
+__device__ __forceinline__ void ssq_add(double &s, int &g, double a) {
+    if (a == 0.0) return;
+    int ga;
+    (void)frexp(a, &ga);
+    if (ga > g) {
+        s = ldexp(s, 2 * (g - ga));
+        g = ga;
+    }
+    double t = ldexp(a, -g);
+    s = s + t * t;
+}
+
+__device__ __forceinline__ void ssq_merge(double &s, int &g, double s2, int g2) {
+    if (g2 > g) {
+        s = ldexp(s, 2 * (g - g2));
+        g = g2;
+    }
+    s = s + ldexp(s2, 2 * (g2 - g));
+}
+
+// floor(P' - 0.5 * (log2(s) + 4 u32)) for s > 0 ([G] Methodik 1), with
+// s = f * 2^E, f in [1,2), E = 2h + q: the argument is
+// (P' - q/2) - (log2 f + 4 u32)/2 - h, so no rounding depends on E.
+__device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
+    int E1;
+    double mnt = frexp(s, &E1);
+    double f = 2.0 * mnt;
+    int E = E1 - 1;
+    int q = E & 1;
+    int h = (E - q) >> 1;
+    double z = (Pp - 0.5 * (double)q) - 0.5 * (log2(f) + 4.0 * kU32);
+    return (int)floor(z) - h;
+}
+
+// Rows of column-major A: thread = row, block column = k-chunk; partial
+// (s, g, nonfinite) per (chunk, row).
+__global__ __launch_bounds__(256) void k_row_norms(const double *__restrict__ A, int64_t m, int64_t k,
+                                                   int64_t lda, int64_t kchunk, double *__restrict__ ps,
+                                                   int *__restrict__ pg, int *__restrict__ pbad) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m) return;
+    int64_t h0 = (int64_t)blockIdx.y * kchunk;
+    int64_t h1 = h0 + kchunk < k ? h0 + kchunk : k;
+    double s = 0.0;
+    int g = kExpEmpty;
+    int bad = 0;
+    const double *a = A + i + h0 * lda;
+    int64_t h = h0;
+    for (; h + 8 <= h1; h += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = a[u * lda];
+        a += 8 * lda;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            double x = fabs(v[u]);
+            if (!(x <= DBL_MAX)) bad = 1;
+            else ssq_add(s, g, x);
+        }
+    }
+    for (; h < h1; ++h, a += lda) {
+        double x = fabs(*a);
+        if (!(x <= DBL_MAX)) bad = 1;
+        else ssq_add(s, g, x);
+    }
+    int64_t o = (int64_t)blockIdx.y * m + i;
+    ps[o] = s;
+    pg[o] = g;
+    pbad[o] = bad;
+}
+
+// Combine the chunks of each row in ascending order; e = fast exponent,
+// ga = max exponent (the r_i of accurate mode). Rows in [m, m_pad) get 0.
+__global__ __launch_bounds__(256) void k_row_exponents(const double *__restrict__ ps, const int *__restrict__ pg,
+                                                       const int *__restrict__ pbad, int64_t m, int64_t m_pad,
+                                                       int nchunks, double Pp, int32_t *__restrict__ e,
+                                                       int32_t *__restrict__ ga) {
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m_pad) return;
+    if (i >= m) {
+        e[i] = 0;
+        ga[i] = 0;
+        return;
+    }
+    double s = 0.0;
+    int g = kExpEmpty;
+    int bad = 0;
+    for (int c = 0; c < nchunks; ++c) {
+        int64_t o = (int64_t)c * m + i;
+        bad |= pbad[o];
+        ssq_merge(s, g, ps[o], pg[o]);
+    }
+    if (bad) {
+        e[i] = kExpNonfinite;
+        ga[i] = kExpNonfinite;
+    } else if (s == 0.0) {
+        e[i] = 0;
+        ga[i] = 0;
+    } else {
+        e[i] = exponent_from_bound(s, Pp) - g;
+        ga[i] = g;
+    }
+}
+
+// Columns of column-major B (contiguous): one wavefront per column, lanes
+// stride the column, then a fixed xor-butterfly merge (every lane ends with
+// the same bits).
+__global__ __launch_bounds__(256) void k_col_exponents(const double *__restrict__ B, int64_t k, int64_t n,
+                                                       int64_t n_pad, int64_t ldb, double Pp,
+                                                       int32_t *__restrict__ f, int32_t *__restrict__ gb) {
+    const int lane = threadIdx.x & 63;
+    int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= n_pad) return;
+    if (j >= n) {
+        if (lane == 0) {
+            f[j] = 0;
+            gb[j] = 0;
+        }
+        return;
+    }
+    const double *col = B + j * ldb;
+    double s = 0.0;
+    int g = kExpEmpty;
+    int bad = 0;
+    int64_t h = lane;
+    for (; h + 3 * 64 < k; h += 4 * 64) {
+        double v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = col[h + 64 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            double x = fabs(v[u]);
+            if (!(x <= DBL_MAX)) bad = 1;
+            else ssq_add(s, g, x);
+        }
+    }
+    for (; h < k; h += 64) {
+        double x = fabs(col[h]);
+        if (!(x <= DBL_MAX)) bad = 1;
+        else ssq_add(s, g, x);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        double s2 = __shfl_xor(s, off, 64);
+        int g2 = __shfl_xor(g, off, 64);
+        bad |= __shfl_xor(bad, off, 64);
+        // the merge is symmetric in its two operands, so both lanes of a pair
+        // end with the same bits
+        ssq_merge(s, g, s2, g2);
+    }
+    if (lane == 0) {
+        if (bad) {
+            f[j] = kExpNonfinite;
+            gb[j] = kExpNonfinite;
+        } else if (s == 0.0) {
+            f[j] = 0;
+            gb[j] = 0;
+        } else {
+            f[j] = exponent_from_bound(s, Pp) - g;
+            gb[j] = g;
+        }
+    }
+}
+
+// Accurate mode: e_i = floor(P' + 6 - r_i - 0.5 (log2 R_i + 4 u32)) with R_i
+// the largest entry of row i of the bound product (0 -> e_i = 0).
+__global__ __launch_bounds__(256) void k_accurate_exponents(const int32_t *__restrict__ rowmax,
+                                                            const int32_t *__restrict__ colmax,
+                                                            const int32_t *__restrict__ ga,
+                                                            const int32_t *__restrict__ gb, int64_t m,
+                                                            int64_t m_pad, int64_t n, int64_t n_pad, double Pp,
+                                                            int32_t *__restrict__ e, int32_t *__restrict__ f) {
+    int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t < m_pad) {
+        int64_t i = t;
+        int v = 0;
+        if (i < m) {
+            if (ga[i] == kExpNonfinite) v = kExpNonfinite;
+            else if (rowmax[i] > 0) v = exponent_from_bound((double)rowmax[i], Pp) + 6 - ga[i];
+        }
+        e[i] = v;
+    } else if (t < m_pad + n_pad) {
+        int64_t j = t - m_pad;
+        int v = 0;
+        if (j < n) {
+            if (gb[j] == kExpNonfinite) v = kExpNonfinite;
+            else if (colmax[j] > 0) v = exponent_from_bound((double)colmax[j], Pp) + 6 - gb[j];
+        }
+        f[j] = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 1 + 2: integerize and split into int8 residues (packed MFMA order)
+// ---------------------------------------------------------------------------
+// Block: 32 rows x 128 columns of K, staged through LDS as doubles so that the
+// global reads are coalesced whichever way the source is laid out. Thread t
+// then owns row (t%64)%32 and 16 consecutive K of fragment block t/64, exactly
+// the 16 bytes lane (t%64) holds in the packed layout.
+constexpr int kSplitRows = 32, kSplitCols = 128, kSplitLd = kSplitCols + 2;
+
+template <bool KCONTIG>
+__device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const double *__restrict__ X,
+                                                int64_t rows, int64_t kdim, int64_t ld, int64_t r0,
+                                                int64_t h0) {
+    const int t = threadIdx.x;
+    if (!KCONTIG) {  // element (r, h) at X[r + h*ld]: rows contiguous
+        const int rr = t & 31, hh = t >> 5;
+        const int64_t r = r0 + rr;
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int hk = hh + 8 * it;
+            const int64_t h = h0 + hk;
+            tile[rr][hk] = (r < rows && h < kdim) ? X[r + h * ld] : 0.0;
+        }
+    } else {  // element (r, h) at X[h + r*ld]: K contiguous
+        const int hh = (t & 63) * 2, rq = t >> 6;
+        const int64_t h = h0 + hh;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int rr = rq + 4 * it;
+            const int64_t r = r0 + rr;
+            double v0 = 0.0, v1 = 0.0;
+            if (r < rows) {
+                const double *src = X + r * ld + h;
+                if (h < kdim) v0 = src[0];
+                if (h + 1 < kdim) v1 = src[1];
+            }
+            tile[rr][hh] = v0;
+            tile[rr][hh + 1] = v1;
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)(d & 0xff) << 24);
+}
+
+template <bool KCONTIG>
+__global__ __launch_bounds__(256) void k_split(const double *__restrict__ X, int64_t rows, int64_t kdim,
+                                               int64_t ld, const int32_t *__restrict__ ex, SplitConsts sc,
+                                               int8_t *__restrict__ out, int64_t plane_bytes, int64_t kb) {
+    __shared__ double tile[kSplitRows][kSplitLd];
+    const int64_t r0 = (int64_t)blockIdx.x * kSplitRows, h0 = (int64_t)blockIdx.y * kSplitCols;
+    split_load_tile<KCONTIG>(tile, X, rows, kdim, ld, r0, h0);
+    __syncthreads();
+
+    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
+    const int kk0 = fb * 32 + 16 * (lane >> 5);
+    const int64_t r = r0 + rr;
+    int e = r < rows ? ex[r] : 0;
+    const bool zero = (e == kExpNonfinite);
+    if (zero) e = 0;
+
+    // x = trunc(a * 2^e) is an integer with |x| < 2^84; split x = d1*2^42 + d0
+    // exactly (|d0| < 2^42). Then x = d1*(2^42 mod p) + d0 (mod p) with that
+    // sum below 2^49.2 in magnitude, so every fma below is exact and
+    // rint(y / p) picks the symmetric residue without ties for odd p.
+    double d0[16], d1[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        double a = zero ? 0.0 : tile[rr][kk0 + u];
+        double x = trunc(ldexp(a, e));
+        double hi = trunc(x * 0x1p-42);
+        d1[u] = hi;
+        d0[u] = fma(-hi, 0x1p42, x);
+    }
+
+    int8_t *dst = out + ((int64_t)blockIdx.x * kb + (int64_t)blockIdx.y * 4 + fb) * 1024 + lane * 16;
+    // modulus 256: x = d0 (mod 256); residue in [-128, 128], 128 and -128 share the low byte
+    {
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = (int)fma(-256.0, rint(d0[u] * 0x1p-8), d0[u]);
+        uint4 w;
+        w.x = pack4(v[0], v[1], v[2], v[3]);
+        w.y = pack4(v[4], v[5], v[6], v[7]);
+        w.z = pack4(v[8], v[9], v[10], v[11]);
+        w.w = pack4(v[12], v[13], v[14], v[15]);
+        *(uint4 *)dst = w;
+    }
+    for (int l = 1; l < sc.n; ++l) {
+        const double p = sc.p[l], pinv = sc.pinv[l], c = sc.c42[l];
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            double y = fma(d1[u], c, d0[u]);
+            v[u] = (int)fma(-p, rint(y * pinv), y);
+        }
+        uint4 w;
+        w.x = pack4(v[0], v[1], v[2], v[3]);
+        w.y = pack4(v[4], v[5], v[6], v[7]);
+        w.z = pack4(v[8], v[9], v[10], v[11]);
+        w.w = pack4(v[12], v[13], v[14], v[15]);
+        *(uint4 *)(dst + l * plane_bytes) = w;
+    }
+}
+
+// Accurate mode: Abar_ih = ceil(|a_ih| * 2^(6 - r_i)) in [0, 64], same packing.
+template <bool KCONTIG>
+__global__ __launch_bounds__(256) void k_quantize(const double *__restrict__ X, int64_t rows, int64_t kdim,
+                                                  int64_t ld, const int32_t *__restrict__ gx,
+                                                  int8_t *__restrict__ out, int64_t kb) {
+    __shared__ double tile[kSplitRows][kSplitLd];
+    const int64_t r0 = (int64_t)blockIdx.x * kSplitRows, h0 = (int64_t)blockIdx.y * kSplitCols;
+    split_load_tile<KCONTIG>(tile, X, rows, kdim, ld, r0, h0);
+    __syncthreads();
+    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
+    const int kk0 = fb * 32 + 16 * (lane >> 5);
+    const int64_t r = r0 + rr;
+    int g = r < rows ? gx[r] : 0;
+    const bool zero = (g == kExpNonfinite);
+    if (zero) g = 0;
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        double a = zero ? 0.0 : fabs(tile[rr][kk0 + u]);
+        v[u] = (int)ceil(ldexp(a, 6 - g));
+    }
+    uint4 w;
+    w.x = pack4(v[0], v[1], v[2], v[3]);
+    w.y = pack4(v[4], v[5], v[6], v[7]);
+    w.z = pack4(v[8], v[9], v[10], v[11]);
+    w.w = pack4(v[12], v[13], v[14], v[15]);
+    *(uint4 *)(out + ((int64_t)blockIdx.x * kb + (int64_t)blockIdx.y * 4 + fb) * 1024 + lane * 16) = w;
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: INT8 GEMM per modulus on v_mfma_i32_32x32x32_i8
+// ---------------------------------------------------------------------------
+// Block tile 256 x 256, four wavefronts in 2 x 2, each owning 128 x 128
+// (4 x 4 MFMA tiles, 256 int32 accumulators per lane). K advances 64 bytes per
+// stage; both operands of a stage (32 fragment blocks, 32 KiB) are copied
+// global -> LDS by global_load_lds_dwordx4 into a double buffer, so the next
+// stage streams in while the current one feeds the MFMAs. The grid runs over
+// (modulus, tile row, tile column); block ids are remapped so that each XCD
+// works through a compact group of tiles of one modulus and its L2 serves the
+// shared A and B panels.
+constexpr int kBK = 64;                    // K bytes per stage
+constexpr int kKS = kBK / 32;              // fragment blocks along K per stage
+constexpr int kFA = (kTileM / 32) * kKS;   // A fragment blocks per stage (16)
+constexpr int kFB = (kTileN / 32) * kKS;   // B fragment blocks per stage (16)
+constexpr int kStageBytes = (kFA + kFB) * 1024;
+constexpr int kGroupM = 4;                 // tile rows per raster group
+
+enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
+
+struct GemmArgs {
+    const int8_t *RA;
+    const int8_t *RB;
+    int64_t planeA, planeB;  // bytes per modulus of RA, RB
+    int64_t kb;              // K / 32
+    int tiles_m, tiles_n, nmod;
+    int64_t m_pad;
+    // epilogues
+    uint8_t *planes;         // EPI_MOD: [nmod][n_pad][m_pad]
+    int32_t *raw;            // EPI_RAW: [nmod][n_pad][m_pad]
+    int32_t *rowmax;         // EPI_BOUND
+    int32_t *colmax;
+    int64_t plane_elems;     // n_pad * m_pad
+};
+
+__device__ __forceinline__ void decode_block(int bid, int total, int tiles_m, int tiles_n, int &l, int &tm,
+                                             int &tn) {
+    // XCD-aware remap: hardware deals consecutive block ids round-robin over
+    // the 8 XCDs; give each XCD one contiguous range of the logical order.
+    int lid = bid;
+    if ((total & 7) == 0) lid = (bid & 7) * (total >> 3) + (bid >> 3);
+    const int per = tiles_m * tiles_n;
+    l = lid / per;
+    int rem = lid - l * per;
+    const int group = kGroupM * tiles_n;
+    const int gid = rem / group;
+    const int first = gid * kGroupM;
+    const int gsz = min(tiles_m - first, kGroupM);
+    const int in = rem - gid * group;
+    tm = first + in % gsz;
+    tn = in / gsz;
+}
+
+__device__ __forceinline__ int mod_u8(int q, double p, double pinv) {
+    // |q| < 2^31: rint(q/p) is the nearest integer for odd p >= 173 (no ties)
+    // and exact for p = 256; r in [-(p-1)/2, (p-1)/2] (or [-128,128]) -> [0, p).
+    double y = (double)q;
+    int r = (int)fma(-p, rint(y * pinv), y);
+    return r < 0 ? r + (int)p : r;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(GemmArgs ga,
+                                                                                         ModConsts mc) {
+    __shared__ __attribute__((aligned(1024))) int8_t lds[2][kStageBytes];
+
+    int l, tm, tn;
+    decode_block(blockIdx.x, gridDim.x, ga.tiles_m, ga.tiles_n, l, tm, tn);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int8_t *gA = ga.RA + (int64_t)l * ga.planeA + (int64_t)tm * (kTileM / 32) * ga.kb * 1024 + lane * 16;
+    const int8_t *gB = ga.RB + (int64_t)l * ga.planeB + (int64_t)tn * (kTileN / 32) * ga.kb * 1024 + lane * 16;
+
+    v16i acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = (v16i){0};
+
+    const int nk = (int)(ga.kb / kKS);
+
+    // Each wave copies 8 of the 32 fragment blocks of a stage.
+    auto load_stage = [&](int ks, int buf) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int fbi = wave * 8 + q;
+            const int8_t *src;
+            if (fbi < kFA) {
+                const int rb = fbi / kKS, kk = fbi % kKS;
+                src = gA + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
+            } else {
+                const int f2 = fbi - kFA;
+                const int rb = f2 / kKS, kk = f2 % kKS;
+                src = gB + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
+            }
+            __builtin_amdgcn_global_load_lds(src, LDS_PTR(&lds[buf][fbi * 1024]), 16, 0, 0);
+        }
+    };
+
+    load_stage(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int ks = 0; ks < nk; ++ks) {
+        const int buf = ks & 1;
+        if (ks + 1 < nk) load_stage(ks + 1, buf ^ 1);
+        const int8_t *sA = &lds[buf][0];
+        const int8_t *sB = &lds[buf][kFA * 1024];
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) {
+            v4i a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *(const v4i *)(sA + ((wm * 4 + i) * kKS + s) * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = *(const v4i *)(sB + ((wn * 4 + j) * kKS + s) * 1024 + lane * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    }
+
+    // Accumulator layout of a 32 x 32 MFMA tile: lane L, register v holds
+    // row 8*(v/4) + 4*(L/32) + v%4, column L%32.
+    const int row_base = tm * kTileM + wm * 128 + 4 * (lane >> 5);
+    const int col_base = tn * kTileN + wn * 128 + (lane & 31);
+    if (EPI == EPI_MOD) {
+        const double p = mc.p[l], pinv = mc.pinv[l];
+        uint8_t *plane = ga.planes + (int64_t)l * ga.plane_elems;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = col_base + 32 * j;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = row_base + 32 * i + 8 * g;
+                    uint32_t w = pack4(mod_u8(acc[i][j][4 * g + 0], p, pinv), mod_u8(acc[i][j][4 * g + 1], p, pinv),
+                                       mod_u8(acc[i][j][4 * g + 2], p, pinv), mod_u8(acc[i][j][4 * g + 3], p, pinv));
+                    *(uint32_t *)(plane + col * ga.m_pad + row) = w;
+                }
+            }
+    } else if (EPI == EPI_RAW) {
+        int32_t *plane = ga.raw + (int64_t)l * ga.plane_elems;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = col_base + 32 * j;
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int row = row_base + 32 * i + 8 * g;
+                    int4 w = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                       acc[i][j][4 * g + 3]);
+                    *(int4 *)(plane + col * ga.m_pad + row) = w;
+                }
+            }
+    } else {  // EPI_BOUND: row and column maxima of the (non-negative) bound product
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                int mx = acc[i][0][v];
+#pragma unroll
+                for (int j = 1; j < 4; ++j) mx = max(mx, acc[i][j][v]);
+                // reduce over the 32 lanes that share this row (same lane/32)
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+                if ((lane & 31) == 0) {
+                    const int row = row_base + 32 * i + 8 * (v >> 2) + (v & 3);
+                    atomicMax(&ga.rowmax[row], mx);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int mx = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = max(mx, acc[i][j][v]);
+            mx = max(mx, __shfl_xor(mx, 32, 64));
+            if (lane < 32) atomicMax(&ga.colmax[col_base + 32 * j], mx);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Steps 4 + 5: CRT in exact 40-bit pieces, symmetric lift, round, unscale
+// ---------------------------------------------------------------------------
+// S = sum_l c_l W_l is kept as four doubles S_t (S = sum_t S_t 2^(40 t)); every
+// term c_l W_l,t < 2^48 and the sums stay below 2^52.4, so they are exact in
+// any order. q = round(S / P) comes from a double estimate; X_t = S_t - q P_t
+// is again exact, carries are propagated, and the rare estimate that lands a
+// hair outside (-P/2, P/2] is corrected on the exact pieces. The integer X is
+// finally rounded to nearest-even from its 160-bit image, so C equals
+// RN(X) * 2^-(e_i + f_j) exactly.
+constexpr double kTwo40 = 0x1p40, kTwoM40 = 0x1p-40;
+
+__device__ __forceinline__ void normalize4(double x[4]) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+        double c = floor(x[t] * kTwoM40);
+        x[t] = fma(-c, kTwo40, x[t]);
+        x[t + 1] += c;
+    }
+}
+
+// sign of a normalized piece vector: -1, 0, +1
+__device__ __forceinline__ int sign4(const double x[4]) {
+    if (x[3] != 0.0) return x[3] > 0.0 ? 1 : -1;
+    return (x[2] != 0.0 || x[1] != 0.0 || x[0] != 0.0) ? 1 : 0;
+}
+
+__device__ double limbs_to_double_rn(const double x[4], int scale_down) {
+    // x normalized and non-negative: x[0..2] in [0, 2^40), x[3] in [0, 2^36)
+    const uint64_t L0 = (uint64_t)x[0], L1 = (uint64_t)x[1], L2 = (uint64_t)x[2], L3 = (uint64_t)x[3];
+    const uint64_t w0 = L0 | (L1 << 40);
+    const uint64_t w1 = (L1 >> 24) | (L2 << 16) | (L3 << 56);
+    const uint64_t w2 = L3 >> 8;
+    uint64_t hi;
+    bool sticky;
+    int scale;  // value = hi * 2^scale + rest, 0 <= rest < 2^scale
+    if (w2) {
+        const int lz = __clzll(w2);
+        hi = lz ? (w2 << lz) | (w1 >> (64 - lz)) : w2;
+        sticky = ((lz ? (w1 << lz) : w1) | w0) != 0;
+        scale = 128 - lz;
+    } else if (w1) {
+        const int lz = __clzll(w1);
+        hi = lz ? (w1 << lz) | (w0 >> (64 - lz)) : w1;
+        sticky = (lz ? (w0 << lz) : w0) != 0;
+        scale = 64 - lz;
+    } else if (w0) {
+        const int lz = __clzll(w0);
+        hi = w0 << lz;
+        sticky = false;
+        scale = -lz;
+    } else {
+        return 0.0;
+    }
+    uint64_t mant = hi >> 11;
+    const uint64_t rb = hi & 0x7ff;
+    if (rb > 0x400 || (rb == 0x400 && (sticky || (mant & 1)))) mant += 1;
+    return ldexp((double)mant, scale + 11 - scale_down);
+}
+
+__device__ double crt_finish(double S[4], int ei, int fj, const CrtConsts &cc) {
+    if (ei == kExpNonfinite || fj == kExpNonfinite) return __builtin_nan("");
+    // S / P estimate (relative error ~2^-51; S/P < 2^13)
+    const double s120 = fma(S[0], 0x1p-120, fma(S[1], 0x1p-80, fma(S[2], kTwoM40, S[3])));
+    const double quo = s120 * cc.pinv120;
+    const double q = rint(quo);
+    double x[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = fma(-q, cc.P[t], S[t]);
+    normalize4(x);
+    if (fabs(quo - q) > 0.5 - 0x1p-30) {
+        // exact check of -P/2 < X <= P/2 on the pieces
+        double z[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) z[t] = x[t] - cc.H[t];
+        normalize4(z);
+        if (sign4(z) > 0) {  // X > P/2
+#pragma unroll
+            for (int t = 0; t < 4; ++t) x[t] -= cc.P[t];
+            normalize4(x);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) z[t] = x[t] + cc.H[t];
+            normalize4(z);
+            if (sign4(z) <= 0) {  // X <= -P/2
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] += cc.P[t];
+                normalize4(x);
+            }
+        }
+    }
+    const bool neg = x[3] < 0.0;
+    if (neg) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = -x[t];
+        normalize4(x);
+    }
+    const double mag = limbs_to_double_rn(x, ei + fj);
+    return neg ? -mag : mag;
+}
+
+// One thread per 4 consecutive rows of one column.
+__global__ __launch_bounds__(256) void k_crt(const uint8_t *__restrict__ planes, int64_t plane_elems,
+                                             int64_t m_pad, int64_t m, int64_t n, const int32_t *__restrict__ e,
+                                             const int32_t *__restrict__ f, CrtConsts cc, double *__restrict__ C,
+                                             int64_t ldc) {
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i0 >= m) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+    double S[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) S[u][t] = 0.0;
+    const uint8_t *src = planes + j * m_pad + i0;
+    for (int l = 0; l < cc.n; ++l) {
+        const uint32_t w = *(const uint32_t *)(src + (int64_t)l * plane_elems);
+        const double w0 = cc.w[l][0], w1 = cc.w[l][1], w2 = cc.w[l][2], w3 = cc.w[l][3];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const double c = (double)((w >> (8 * u)) & 0xffu);
+            S[u][0] = fma(c, w0, S[u][0]);
+            S[u][1] = fma(c, w1, S[u][1]);
+            S[u][2] = fma(c, w2, S[u][2]);
+            S[u][3] = fma(c, w3, S[u][3]);
+        }
+    }
+    const int fj = f[j];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = i0 + u;
+        if (i < m) C[i + j * ldc] = crt_finish(S[u], e[i], fj, cc);
+    }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small helpers
+// ---------------------------------------------------------------------------
+__global__ void k_fill_i32(int32_t *p, int64_t count, int32_t v) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = v;
+}
+
+__global__ void k_zero_c(double *C, int64_t m, int64_t n, int64_t ldc) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= m) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) C[i + j * ldc] = 0.0;
+}
+
+// packed [l][rows_pad/32][kb][64][16] -> logical [l][rows][k]
+__global__ void k_unpack(const int8_t *packed, int64_t rows, int64_t k, int64_t plane_bytes, int64_t kb,
+                         int8_t *out) {
+    const int64_t h = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t l = blockIdx.z;
+    if (h >= k) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const int64_t lane = (r & 31) + 32 * ((h & 31) >> 4);
+        const int64_t off = (((r >> 5) * kb + (h >> 5)) * 64 + lane) * 16 + (h & 15);
+        out[(l * rows + r) * k + h] = packed[l * plane_bytes + off];
+    }
+}
+
+template <typename T>
+__global__ void k_copy_planes(const T *planes, int64_t m, int64_t m_pad, int64_t plane_elems, int64_t n,
+                              T *out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t l = blockIdx.z;
+    if (i >= m) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) out[(l * n + j) * m + i] = planes[l * plane_elems + j * m_pad + i];
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count + per - 1) / per); }
+static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
+
+hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L, char *ws,
+                            hipStream_t s) {
+    dim3 grid(nblk(m, 256), (unsigned)L.nchunks);
+    hipLaunchKernelGGL(k_row_norms, grid, dim3(256), 0, s, A, m, k, lda, L.kchunk, (double *)(ws + L.part_s),
+                       (int *)(ws + L.part_g), (int *)(ws + L.part_bad));
+    return hipGetLastError();
+}
+
+hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_row_exponents, dim3(nblk(L.m_pad, 256)), dim3(256), 0, s, (const double *)(ws + L.part_s),
+                       (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad), m, L.m_pad, L.nchunks, Pp,
+                       (int32_t *)(ws + L.e), (int32_t *)(ws + L.ga));
+    return hipGetLastError();
+}
+
+hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp, const Layout &L,
+                                char *ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_col_exponents, dim3(nblk(L.n_pad, 4)), dim3(256), 0, s, B, k, n, L.n_pad, ldb, Pp,
+                       (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
+    return hipGetLastError();
+}
+
+hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                        const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad, const Layout &L,
+                        hipStream_t s) {
+    dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
+    const int64_t plane = rows_pad * L.k_pad;
+    if (k_contiguous)
+        hipLaunchKernelGGL(k_split<true>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
+    else
+        hipLaunchKernelGGL(k_split<false>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L, hipStream_t s) {
+    dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
+    if (k_contiguous)
+        hipLaunchKernelGGL(k_quantize<true>, grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
+    else
+        hipLaunchKernelGGL(k_quantize<false>, grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s) {
+    if (count <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_i32, dim3(nblk(count, 256)), dim3(256), 0, s, p, count, value);
+    return hipGetLastError();
+}
+
+static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, const Layout &L) {
+    GemmArgs g{};
+    g.RA = RA;
+    g.RB = RB;
+    g.planeA = L.m_pad * L.k_pad;
+    g.planeB = L.n_pad * L.k_pad;
+    g.kb = L.kb;
+    g.tiles_m = (int)(L.m_pad / kTileM);
+    g.tiles_n = (int)(L.n_pad / kTileN);
+    g.nmod = nmod;
+    g.m_pad = L.m_pad;
+    g.plane_elems = L.m_pad * L.n_pad;
+    return g;
+}
+
+hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc, uint8_t *planes,
+                           const Layout &L, hipStream_t s) {
+    GemmArgs g = gemm_args(RA, RB, nmod, L);
+    g.planes = planes;
+    const int blocks = g.tiles_m * g.tiles_n * nmod;
+    hipLaunchKernelGGL(k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw, const Layout &L,
+                           hipStream_t s) {
+    GemmArgs g = gemm_args(RA, RB, nmod, L);
+    g.raw = raw;
+    ModConsts mc{};
+    const int blocks = g.tiles_m * g.tiles_n * nmod;
+    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(256), 0, s, g, mc);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
+                             const Layout &L, hipStream_t s) {
+    GemmArgs g = gemm_args(Abar, Bbar, 1, L);
+    g.rowmax = rowmax;
+    g.colmax = colmax;
+    ModConsts mc{};
+    const int blocks = g.tiles_m * g.tiles_n;
+    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(256), 0, s, g, mc);
+    return hipGetLastError();
+}
+
+hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws, hipStream_t s) {
+    hipLaunchKernelGGL(k_accurate_exponents, dim3(nblk(L.m_pad + L.n_pad, 256)), dim3(256), 0, s,
+                       (const int32_t *)(ws + L.rowmax), (const int32_t *)(ws + L.colmax),
+                       (const int32_t *)(ws + L.ga), (const int32_t *)(ws + L.gb), m, L.m_pad, n, L.n_pad, Pp,
+                       (int32_t *)(ws + L.e), (int32_t *)(ws + L.f));
+    return hipGetLastError();
+}
+
+hipError_t launch_crt(const uint8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s) {
+    dim3 grid(nblk((m + 3) / 4, 256), ydim(n));
+    hipLaunchKernelGGL(k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_c, dim3(nblk(m, 256), ydim(n)), dim3(256), 0, s, C, m, n, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k, int64_t rows_pad,
+                                  const Layout &L, int8_t *out, hipStream_t s) {
+    dim3 grid(nblk(k, 256), ydim(rows), (unsigned)nmod);
+    hipLaunchKernelGGL(k_unpack, grid, dim3(256), 0, s, packed, rows, k, rows_pad * L.k_pad, L.kb, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_planes_u8(const uint8_t *planes, int nmod, int64_t m, int64_t n, const Layout &L,
+                                 uint8_t *out, hipStream_t s) {
+    dim3 grid(nblk(m, 256), ydim(n), (unsigned)nmod);
+    hipLaunchKernelGGL(k_copy_planes<uint8_t>, grid, dim3(256), 0, s, planes, m, L.m_pad, L.m_pad * L.n_pad, n, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
+                                  int32_t *out, hipStream_t s) {
+    dim3 grid(nblk(m, 256), ydim(n), (unsigned)nmod);
+    hipLaunchKernelGGL(k_copy_planes<int32_t>, grid, dim3(256), 0, s, raw, m, L.m_pad, L.m_pad * L.n_pad, n, out);
+    return hipGetLastError();
+}
+
+}  // namespace oz2

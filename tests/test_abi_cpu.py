@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, validates arguments before touching the device, and its own
+tables agree with the oracle's independently built ones."""
+import math
+import os
+import re
+
+import pytest
+
+import oracle as O
+import rns_emulated_fp64_amd as oz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ozaki2.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ozaki2_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = oz.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    assert sorted(oz.EXPORTS) == names
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_nm_lists_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", oz.LIB_PATH], capture_output=True, text=True).stdout
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_moduli_and_constants_match_oracle():
+    assert oz.ozaki2_max_moduli() == 20
+    for n in range(2, 21):
+        mods = oz.ozaki2_moduli(n)
+        assert mods == O.choose_moduli(n)
+        t = O.crt_tables(mods)
+        assert oz.ozaki2_scaling_constant(n) == O.scaling_constant(t["P"]), n
+        for l in range(n):
+            assert oz.ozaki2_crt_weight(n, l) == t["W"][l]
+
+
+def test_host_argument_errors():
+    L = oz.lib()
+    with pytest.raises(oz.Ozaki2Error):
+        oz.ozaki2_moduli(0)
+    with pytest.raises(oz.Ozaki2Error):
+        oz.ozaki2_scaling_constant(21)
+    assert L.ozaki2_moduli(3, None) == -2
+    assert L.ozaki2_crt_weight(8, 8, None, 8) == -2
+
+
+P = 1 << 20  # a fake non-null pointer: validation fails before it is ever used
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((-1, 4, 4, P, 4, P, 4, P, 4, 8, 0), -1),
+        ((4, -1, 4, P, 4, P, 4, P, 4, 8, 0), -2),
+        ((4, 4, -1, P, 4, P, 4, P, 4, 8, 0), -3),
+        ((4, 4, 4, 0, 4, P, 4, P, 4, 8, 0), -4),
+        ((4, 4, 4, P, 3, P, 4, P, 4, 8, 0), -5),
+        ((4, 4, 4, P, 4, 0, 4, P, 4, 8, 0), -6),
+        ((4, 4, 4, P, 4, P, 3, P, 4, 8, 0), -7),
+        ((4, 4, 4, P, 4, P, 4, 0, 4, 8, 0), -8),
+        ((4, 4, 4, P, 4, P, 4, P, 3, 8, 0), -9),
+        ((4, 4, 4, P, 4, P, 4, P, 4, 1, 0), -10),
+        ((4, 4, 4, P, 4, P, 4, P, 4, 21, 0), -10),
+        ((4, 4, 4, P, 4, P, 4, P, 4, 8, 2), -11),
+        ((4, 4, 4, P, 4, P, 4, P, 4, 8, -1), -11),
+        ((4, 4, 1 << 17, P, 4, P, 1 << 17, P, 4, 8, 0), 3),
+        # quick returns: nothing is launched for an empty C
+        ((0, 4, 4, 0, 1, P, 4, 0, 1, 8, 0), 0),
+        ((4, 0, 4, P, 4, 0, 4, 0, 4, 8, 0), 0),
+    ],
+)
+def test_status_codes(args, status):
+    assert oz.ozaki2_dgemm(*args, 0) == status
+    assert oz.ozaki2_dgemm_ws(*args, P, 1 << 40, 0) == status
+
+
+def test_workspace_checks():
+    assert oz.ozaki2_dgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, 0, 0, 0) == -12
+    need = oz.ozaki2_workspace_size(64, 64, 64, 8, 0)
+    assert need > 0
+    assert oz.ozaki2_dgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, P, need - 1, 0) == 2
+    assert oz.ozaki2_workspace_size(0, 4, 4, 8, 0) == 0
+    assert oz.ozaki2_workspace_size(4, 4, 4, 1, 0) == 0
+    # residues dominate: N * (m_pad + n_pad) * k_pad + N * m_pad * n_pad bytes
+    ws = oz.ozaki2_workspace_size(4096, 4096, 4096, 16, 0)
+    assert 16 * (2 * 4096 * 4096 + 4096 * 4096) <= ws < 16 * 3 * 4096 * 4096 * 1.05
+    assert oz.ozaki2_workspace_size(4096, 4096, 4096, 16, 1) > ws
+    assert oz.ozaki2_debug_workspace_size(300, 200, 500, 8, 0) > oz.ozaki2_workspace_size(300, 200, 500, 8, 0)
+
+
+def test_status_strings():
+    for s in (0, 1, 2, 3, -4, 99):
+        assert isinstance(oz.status_string(s), str) and oz.status_string(s)

@@ -1,0 +1,216 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar: exponents equal (with the documented boundary protocol), int8 residues,
+int32 residue products and reduced residues bit-exact, and C bit-exact: the
+GPU reconstructs the exact integer and rounds it once to nearest-even, the
+same RN(X) * 2^-(e_i + f_j) the oracle computes with Python integers.
+
+Pages: [Q] the Qiita article on Ozaki Scheme II (steps 1-5); [G] "Improved
+Scaling for Fast Mode of Ozaki Scheme II" (section Methodik).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_bitwise_equal, full_parity, run_debug, run_ws, stream_handle, device_colmajor
+import rns_emulated_fp64_amd as oz
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oz.lib()
+
+
+def test_config_u64_n8():
+    # 64^3, U(-1,1), N = 8, fast mode
+    A, B = W.make("u64_n8")
+    g, r, mism = full_parity(A, B, 8)
+    assert mism == 0
+
+
+@pytest.mark.parametrize("N", [2, 8, 14, 16, 18, 20])
+def test_ragged_several_tiles_fast(N):
+    # m, n span two 256-row/column tiles and k a ragged 128-wide tail
+    A, B = W.spread_case(300, 290, 500, 1.0, seed=N)
+    full_parity(A, B, N)
+
+
+@pytest.mark.parametrize("N", [8, 14, 16, 20])
+def test_ragged_accurate(N):
+    A, B = W.spread_case(270, 333, 260, 1.5, seed=100 + N)
+    full_parity(A, B, N, "accurate")
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 7, 3), (5, 1, 200), (33, 17, 129), (64, 64, 1)])
+def test_tiny_shapes(shape):
+    m, n, k = shape
+    A, B = W.uniform_case(m, n, k, seed=m * 7 + k)
+    full_parity(A, B, 14)
+    full_parity(A, B, 16, "accurate")
+
+
+def test_leading_dimensions():
+    A, B = W.spread_case(257, 130, 190, 0.5, seed=3)
+    g, r, _ = full_parity(A, B, 16, lda=263, ldb=200, ldc=300)
+    # entries beyond m in each column of C are left alone
+    pad = g["C_padding"][:130, 257:]
+    assert np.all(np.isnan(pad))
+
+
+def test_max_inner_dimension():
+    # k = 2^17 - 1, the largest k for which int32 sums stay exact ([Q] step 3)
+    k = (1 << 17) - 1
+    A, B = W.uniform_case(6, 5, k, seed=4)
+    A[0] = 1.0
+    B[:, 0] = -1.0
+    full_parity(A, B, 16, want_prod=True)
+
+
+def test_special_values_and_zero_lines():
+    A, B = W.spread_case(70, 66, 90, 1.0, seed=5)
+    A[3] = 0.0
+    B[:, 5] = 0.0
+    A[7, 11] = np.inf
+    A[9, 2] = np.nan
+    B[4, 8] = -np.inf
+    A[20] *= 2.0 ** 900
+    A[21] *= 2.0 ** -900
+    B[:, 30] *= 2.0 ** -1000   # subnormal entries
+    A[40, :] = 0.0
+    A[40, 17] = 5e-324         # a lone subnormal
+    g, r, _ = full_parity(A, B, 16)
+    C = g["C"]
+    assert np.all(np.isnan(C[7])) and np.all(np.isnan(C[9])) and np.all(np.isnan(C[:, 8]))
+    assert np.all(C[3, [j for j in range(66) if j != 8]] == 0.0)
+    full_parity(A, B, 14, "accurate")
+
+
+def test_k_zero_and_empty():
+    dA = torch.zeros(1, dtype=torch.float64, device="cuda")
+    dC = torch.full((4, 5), float("nan"), dtype=torch.float64, device="cuda")
+    st = oz.ozaki2_dgemm(5, 4, 0, dA.data_ptr(), 5, dA.data_ptr(), 1, dC.data_ptr(), 5, 16, 0, stream_handle())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.all(dC == 0)
+    dC.fill_(float("nan"))
+    st = oz.ozaki2_dgemm(0, 4, 3, dA.data_ptr(), 1, dA.data_ptr(), 3, dC.data_ptr(), 1, 16, 0, stream_handle())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(dC))
+
+
+def test_cached_workspace_entry_and_determinism():
+    A, B = W.spread_case(400, 300, 700, 1.0, seed=6)
+    dA, dB = device_colmajor(A), device_colmajor(B)
+    outs = []
+    for _ in range(2):
+        dC = torch.empty((300, 400), dtype=torch.float64, device="cuda")
+        st = oz.ozaki2_dgemm(400, 300, 700, dA.data_ptr(), 400, dB.data_ptr(), 700, dC.data_ptr(), 400, 16, 0,
+                             stream_handle())
+        assert st == 0
+        outs.append(dC.cpu().numpy().T.copy())
+    assert_bitwise_equal(outs[0], outs[1], "rerun")
+    r = O.os2_dgemm(A, B, 16)
+    assert_bitwise_equal(outs[0], r["C"], "C via ozaki2_dgemm")
+    # a different, larger problem grows the cached workspace
+    A2, B2 = W.spread_case(600, 520, 900, 1.0, seed=7)
+    dA2, dB2 = device_colmajor(A2), device_colmajor(B2)
+    dC2 = torch.empty((520, 600), dtype=torch.float64, device="cuda")
+    assert oz.ozaki2_dgemm(600, 520, 900, dA2.data_ptr(), 600, dB2.data_ptr(), 900, dC2.data_ptr(), 600, 14, 1,
+                           stream_handle()) == 0
+    assert_bitwise_equal(dC2.cpu().numpy().T.copy(), O.os2_dgemm(A2, B2, 14, "accurate")["C"], "grown ws")
+
+
+def test_non_default_stream():
+    A, B = W.spread_case(128, 96, 256, 1.0, seed=8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = oz.dgemm(torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), 16)
+    s.synchronize()
+    r = O.os2_dgemm(B.T, A.T, 16)  # the binding multiplies B^T A^T in column-major terms
+    assert_bitwise_equal(C.cpu().numpy(), r["C"].T, "torch wrapper")
+
+
+def test_config_spread05_1024_n14():
+    # 1024^3, phi = 0.5, N = 14: full parity and the accuracy gate
+    A, B = W.make("spread0.5_1024_n14")
+    g, r, mism = full_parity(A, B, 14, want_prod=False)
+    hi, lo = O.dd_gemm(A, B)
+    err = O.error_metrics(g["C"], hi, lo, A, B)
+    native = O.error_metrics(A @ B, hi, lo, A, B)
+    print("1024^3 N=14:", err, "native:", native, "exponent mismatches:", mism)
+    assert err["E_cw"] <= 1e-14
+
+
+def _sampled_exact_check(A, B, C, e, f, rows, cols):
+    """C[i, j] == RN(exact scaled dot) * 2^-(e_i + f_j) on sampled entries."""
+    Ai = O.scaled_integers(A[rows], [e[i] for i in rows])
+    Bi = O.scaled_integers(np.asarray(B)[:, cols].T, [f[j] for j in cols])
+    Y = Ai.dot(Bi.T)
+    ref = O.unscale(Y, [e[i] for i in rows], [f[j] for j in cols])
+    assert_bitwise_equal(C[np.ix_(rows, cols)], ref, "sampled C")
+
+
+@pytest.mark.parametrize("mode", ["fast", "accurate"])
+def test_config_spread1_4096_n16(mode):
+    # The headline workload at full size, in the configuration the benchmark times.
+    A, B = W.make("spread1.0_4096_n16")
+    N = 16
+    g = run_debug(A, B, N, mode, want_prod=False)
+    e = g["e"].tolist()
+    f = g["f"].tolist()
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(4096, 24, replace=False)).tolist()
+    cols = np.sort(rng.choice(4096, 24, replace=False)).tolist()
+    # exponents of the sampled rows/columns against the oracle (protocol on mismatch)
+    Pp = O.scaling_constant(math.prod(O.choose_moduli(N)))
+    if mode == "fast":
+        oe = O.fast_exponents_rows(A[rows], Pp)
+        of = O.fast_exponents_rows(B[:, cols].T, Pp)
+        assert sum(a != b for a, b in zip(oe, [e[i] for i in rows])) <= 1
+        assert sum(a != b for a, b in zip(of, [f[j] for j in cols])) <= 1
+    else:
+        oe, of = O.exponents(A, B, N, "accurate")
+        assert oe == e and of == f
+    # residues of sampled rows, bit-exact
+    mods = O.choose_moduli(N)
+    assert np.array_equal(g["RA"][:, rows, :], O.split(A[rows], [e[i] for i in rows], mods))
+    assert np.array_equal(g["RB"][:, cols, :], O.split(B[:, cols].T, [f[j] for j in cols], mods))
+    # reduced products on sampled entries
+    RA = g["RA"][:, rows, :].astype(np.int64)
+    RB = g["RB"][:, cols, :].astype(np.int64)
+    for l, p in enumerate(mods):
+        Q = RA[l] @ RB[l].T
+        assert np.array_equal(np.mod(Q, p), g["red"][l][np.ix_(cols, rows)].T)
+    # C bit-exact on sampled entries, and the launch configuration of the benchmark agrees
+    _sampled_exact_check(A, B, g["C"], e, f, rows, cols)
+    C_ws = run_ws(A, B, N, mode)
+    assert_bitwise_equal(C_ws, g["C"], "ws vs debug")
+    hi, lo = O.dd_gemm(A[rows], B)
+    err = O.error_metrics(g["C"][rows], hi, lo, A[rows], B)
+    print(f"4096^3 N=16 {mode}:", err)
+    assert err["E_cw"] <= 1e-14
+
+
+def test_config_scale_sweep_2048_n14():
+    # A = alpha*ones and alpha*U(-1,1), alpha = 2^s: C(alpha) == alpha*C(1) bit
+    # for bit and CRT succeeds at every alpha ([G] Methodik 2, Problemstellung).
+    ones, ua, B = W.scale_sweep_case(2048)
+    rng = np.random.default_rng(2)
+    rows = np.sort(rng.choice(2048, 8, replace=False)).tolist()
+    cols = np.sort(rng.choice(2048, 8, replace=False)).tolist()
+    for A in (ones, ua):
+        base = run_debug(A, B, 14, want_prod=False, want_res=False)
+        for s in (-64, -32, 0, 32, 64):
+            As = np.ldexp(A, s)
+            g = run_debug(As, B, 14, want_prod=False, want_res=False)
+            assert np.array_equal(g["e"], base["e"] - s)
+            assert_bitwise_equal(g["C"], np.ldexp(base["C"], s), f"scale 2^{s}")
+        _sampled_exact_check(A, B, base["C"], base["e"].tolist(), base["f"].tolist(), rows, cols)
