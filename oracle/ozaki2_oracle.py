@@ -264,6 +264,10 @@ def accurate_bound_operands(A: np.ndarray, B: np.ndarray):
     """
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
+    # Rows of A / columns of B holding Inf or NaN become NaN lines of C
+    # whatever the exponents; they take no part in the bound product.
+    A = np.where(np.all(np.isfinite(A), axis=1)[:, None], A, 0.0)
+    B = np.where(np.all(np.isfinite(B), axis=0)[None, :], B, 0.0)
     ra = _frexp_exponent(np.max(np.abs(A), axis=1)) if A.shape[1] else np.zeros(A.shape[0], np.int64)
     cb = _frexp_exponent(np.max(np.abs(B), axis=0)) if B.shape[0] else np.zeros(B.shape[1], np.int64)
     abar = np.ceil(np.ldexp(np.abs(A), (6 - ra)[:, None]))

@@ -327,6 +327,12 @@ def test_zero_rows_and_nonfinite():
     good = np.ix_([0, 2, 4, 5], [0, 1, 3])
     hi, lo = O.dd_gemm(A[[0, 2, 4, 5]], B[:, [0, 1, 3]])
     assert np.max(np.abs(C[good] - hi)) < 1e-14
+    # accurate mode: the Inf/NaN lines take no part in the bound product
+    ra = O.os2_dgemm(A, B, 14, "accurate")
+    assert ra["e"][3] is None and ra["f"][4] is None
+    assert all(v is not None for i, v in enumerate(ra["e"]) if i != 3)
+    assert np.all(np.isnan(ra["C"][3])) and np.all(np.isnan(ra["C"][:, 4]))
+    assert np.max(np.abs(ra["C"][good] - hi)) < 1e-14
 
 
 def test_dd_gemm_against_exact_fractions():
