@@ -1,0 +1,195 @@
+"""Benchmark of the Ozaki Scheme II FP64 GEMM emulation on one MI355X.
+
+One step = one ozaki2_dgemm_ws call (all phases: exponents, residue split,
+INT8 GEMMs, CRT + unscale) on operands already resident in HBM. Prints ONE
+JSON line; see the design doc for the roofline and cpu_baseline definitions.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                       [--mode fast|accurate] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA (no sparsity)
+FP64_PEAK_TFLOPS = 78.6      # MI355X FP64 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="spread1.0_4096_n16")
+    p.add_argument("--mode", default="fast", choices=["fast", "accurate"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true", help="skip the accurate-mode and native-FP64 context runs")
+    p.add_argument("--cpu-rows", type=int, default=0, help="rows of A in the oracle sample (0: automatic)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def time_steps(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
+    """The oracle (as it stands) on a bounded sample: the first rows of A times all of B."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    omp_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    m, k = A.shape
+    n = B.shape[1]
+    rows = rows_wanted or max(8, min(m, int(1536 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
+    rows = min(rows, m)
+    log(f"cpu_baseline: oracle on {rows} rows x {n} columns, k={k}, N={N}, {mode}")
+    t0 = time.perf_counter()
+    r = O.os2_dgemm(A[:rows], B, N, mode)
+    t = time.perf_counter() - t0
+    value = 2.0 * rows * n * k / t / 1e12
+    Cs = C_gpu[:rows]
+    diff = (Cs.view(np.uint64) != r["C"].view(np.uint64)) & ~(np.isnan(Cs) & np.isnan(r["C"]))
+    er = min(rows, 128)  # accuracy against the double-double reference on the first rows
+    hi, lo = O.dd_gemm(A[:er], B)
+    err = O.error_metrics(Cs[:er], hi, lo, A[:er], B)
+    native = O.error_metrics(A[:er] @ B, hi, lo, A[:er], B)
+    return dict(value=value, unit="TFLOPS", cores=max(omp_threads, blas_threads), kind="oracle",
+                sample=f"rows 0..{rows - 1} of A times all of B ({rows}x{n}x{k}, N={N}, {mode}); "
+                       f"{t:.2f} s; OpenMP {omp_threads} threads, BLAS {blas_threads} threads"), \
+        dict(parity_mismatches=int(diff.sum()), parity_entries=int(Cs.size), error_rows=er, **err,
+             native_fp64_E_cw=native["E_cw"], native_fp64_E_el=native["E_el"])
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the product would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rns_emulated_fp64_amd as oz
+    import workloads as W
+
+    cfg = W.CONFIGS[args.config]
+    if cfg["kind"] == "sweep":
+        raise SystemExit("the scale sweep is a parity-test case, not a bench line")
+    m, n, k, N = cfg["m"], cfg["n"], cfg["k"], cfg["num_moduli"]
+    md = oz.MODES[args.mode]
+    log(f"generating {args.config} ({m}x{k} @ {k}x{n}), N={N}, mode={args.mode}")
+    A, B = W.make(args.config)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)  # column-major A, lda = m
+    dB = torch.from_numpy(np.ascontiguousarray(B.T)).to(dev)  # column-major B, ldb = k
+    dC = torch.empty((n, m), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def workspace(mode_id):
+        wb = oz.ozaki2_workspace_size(m, n, k, N, mode_id)
+        return torch.empty(wb, dtype=torch.uint8, device=dev), wb
+
+    ws, wbytes = workspace(md)
+
+    def step(mode_id=md, w=None, wb=None):
+        w = ws if w is None else w
+        wb = wbytes if wb is None else wb
+        st = oz.ozaki2_dgemm_ws(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, mode_id,
+                                w.data_ptr(), wb, stream)
+        if st:
+            raise RuntimeError(oz.status_string(st))
+
+    # timed region: K steps, per-phase HIP events recorded on the same stream
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    oz.ozaki2_timing_enable(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    phase_ms, calls = oz.ozaki2_timing_read()
+    oz.ozaki2_timing_enable(0)
+    phase_avg = {p: v / max(calls, 1) for p, v in phase_ms.items()}
+    log(f"{ms:.3f} ms/step; phases {phase_avg}")
+
+    flops = 2.0 * m * n * k
+    tflops = flops / (ms * 1e-3) / 1e12
+    int8_ops = N * flops  # one INT8 GEMM per modulus, all in one launch
+    gemm_tops = int8_ops / (phase_avg["gemm"] * 1e-3) / 1e12
+    roofline = dict(bound="mfma", achieved=round(gemm_tops, 2), peak=INT8_PEAK_TOPS, unit="TFLOP/s",
+                    frac=round(gemm_tops / INT8_PEAK_TOPS, 4), traffic=None,
+                    kernel="k_gemm<EPI_MOD>", ops_per_launch=int8_ops, dtype="int8")
+
+    C = dC.cpu().numpy().T  # C of the last step
+    extras = {}
+    if not args.no_extras:
+        # accurate mode (the other mode) and native FP64 on the same operands, as context
+        other = "accurate" if args.mode == "fast" else "fast"
+        w2, wb2 = workspace(oz.MODES[other])
+        ms2 = time_steps(lambda: step(oz.MODES[other], w2, wb2), max(args.steps // 2, 3), 2, torch)
+        extras[f"{other}_mode_tflops"] = round(flops / (ms2 * 1e-3) / 1e12, 3)
+        extras[f"{other}_mode_ms_per_step"] = round(ms2, 4)
+        del w2
+        step()  # restore C of the benchmarked mode
+        torch.cuda.synchronize()
+        At = torch.from_numpy(A).to(dev)
+        Bt = torch.from_numpy(B).to(dev)
+        ms3 = time_steps(lambda: torch.mm(At, Bt), max(args.steps // 2, 3), 2, torch)
+        extras["native_fp64_gemm_tflops"] = round(flops / (ms3 * 1e-3) / 1e12, 3)
+        del At, Bt
+
+    cpu = None
+    accuracy = None
+    if not args.no_cpu_baseline:
+        cpu, accuracy = cpu_baseline_leg(A, B, C, N, args.mode, args.cpu_rows)
+
+    line = dict(
+        metric="emulated FP64 TFLOPS (2mnk/t) at 4096^3, % INT8 MFMA peak; max rel err",
+        value=round(tflops, 3), unit="TFLOPS", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="int8", data="synthetic",
+        config=dict(workload=args.config, m=m, n=n, k=k, num_moduli=N, mode=args.mode,
+                    entries=("(U(0,1)-0.5)*exp(%s*N(0,1))" % cfg.get("phi")) if cfg["kind"] == "spread"
+                    else "U(-1,1)", seed=cfg["seed"]),
+        emulated_vs_fp64_peak=round(tflops / FP64_PEAK_TFLOPS, 3),
+        gemm_int8_peak_frac=roofline["frac"],
+        phase_ms={p: round(v, 4) for p, v in phase_avg.items()},
+        roofline=roofline,
+        cpu_baseline=cpu,
+        accuracy=accuracy,
+        **extras,
+    )
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
