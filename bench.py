@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the accurate-mode and native-FP64 context runs")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of A in the oracle sample (0: automatic)")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="only run a plain device copy of this many MiB (3 times) for HBM counter calibration")
     return p.parse_args()
 
 
@@ -94,6 +96,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy_mib:
+        # a plain copy kernel of known size: reads and writes exactly this many bytes
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 8, dtype=torch.float64, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps(dict(calibration="copy", bytes_read=nbytes, bytes_written=nbytes, launches=3)))
+        return
 
     import rns_emulated_fp64_amd as oz
     import workloads as W

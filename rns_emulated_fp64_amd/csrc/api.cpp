@@ -166,11 +166,11 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
 
     // Step 3: one exact INT8 product per modulus, reduced mod p_l.
     HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, T->mod,
-                            (uint8_t *)(ws + L.planes), L, s));
+                            (int8_t *)(ws + L.planes), L, s));
     if (ev) HIP_TRY(hipEventRecord(ev[3], s));
 
     // Steps 4 + 5: reconstruction and unscaling.
-    HIP_TRY(launch_crt((const uint8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s));
+    HIP_TRY(launch_crt((const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s));
     if (ev) HIP_TRY(hipEventRecord(ev[4], s));
 
     if (dbg) {
@@ -181,7 +181,7 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
         if (dbg->rb)
             HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.rb), nmod, n, k, L.n_pad, L, dbg->rb, s));
         if (dbg->red)
-            HIP_TRY(launch_copy_planes_u8((const uint8_t *)(ws + L.planes), nmod, m, n, L, dbg->red, s));
+            HIP_TRY(launch_copy_planes_u8((const int8_t *)(ws + L.planes), nmod, T->mod, m, n, L, dbg->red, s));
         if (dbg->prod) {
             HIP_TRY(launch_gemm_raw((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod,
                                     (int32_t *)(ws + L.raw), L, s));

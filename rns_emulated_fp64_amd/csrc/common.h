@@ -61,7 +61,7 @@ struct Layout {
     size_t rowmax, colmax;            // int32 [m_pad], [n_pad] (accurate mode)
     size_t abar, bbar;                // int8 packed bound operands (accurate mode)
     size_t ra, rb;                    // int8 packed residues [N][m_pad][k_pad], [N][n_pad][k_pad]
-    size_t planes;                    // uint8 [N][n_pad][m_pad]: products mod p
+    size_t planes;                    // int8 [N][n_pad][m_pad]: products mod p, symmetric range
     size_t raw;                       // int32 [N][n_pad][m_pad] (debug only)
     size_t total;
 };
@@ -82,20 +82,20 @@ hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld,
                            hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc,
-                           uint8_t *planes, const Layout &L, hipStream_t s);
+                           int8_t *planes, const Layout &L, hipStream_t s);
 hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw,
                            const Layout &L, hipStream_t s);
 hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
                              const Layout &L, hipStream_t s);
 hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws,
                                      hipStream_t s);
-hipError_t launch_crt(const uint8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s);
 hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
 hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
-hipError_t launch_copy_planes_u8(const uint8_t *planes, int nmod, int64_t m, int64_t n, const Layout &L,
-                                 uint8_t *out, hipStream_t s);
+hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,
+                                 const Layout &L, uint8_t *out, hipStream_t s);
 hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
                                   int32_t *out, hipStream_t s);
 

@@ -370,18 +370,25 @@ __global__ __launch_bounds__(256) void k_quantize(const double *__restrict__ X, 
 // ---------------------------------------------------------------------------
 // Block tile 256 x 256, four wavefronts in 2 x 2, each owning 128 x 128
 // (4 x 4 MFMA tiles, 256 int32 accumulators per lane). K advances 64 bytes per
-// stage; both operands of a stage (32 fragment blocks, 32 KiB) are copied
-// global -> LDS by global_load_lds_dwordx4 into a double buffer, so the next
-// stage streams in while the current one feeds the MFMAs. The grid runs over
-// (modulus, tile row, tile column); block ids are remapped so that each XCD
-// works through a compact group of tiles of one modulus and its L2 serves the
-// shared A and B panels.
+// LDS stage (two 32-wide substeps). Stages are copied global -> LDS with
+// global_load_lds_dwordx4 (no VGPR staging) into a ring of kNST buffers, so up
+// to kNST-1 stages are in flight while the MFMAs consume the oldest one.
+// Fragments are double-buffered in registers: the reads for the next substep
+// are issued before the 16 MFMAs of the current one, and the block barrier of
+// a stage is taken before the last substep's MFMAs, whose operands are
+// already in registers. The grid runs over (modulus, tile row, tile column);
+// block ids are remapped so each XCD works through a compact group of tiles of
+// one modulus and its L2 serves the shared A and B panels.
 constexpr int kBK = 64;                    // K bytes per stage
-constexpr int kKS = kBK / 32;              // fragment blocks along K per stage
+constexpr int kKS = kBK / 32;              // 32-wide substeps per stage
+constexpr int kNST = 4;                    // LDS stages in the ring
 constexpr int kFA = (kTileM / 32) * kKS;   // A fragment blocks per stage (16)
 constexpr int kFB = (kTileN / 32) * kKS;   // B fragment blocks per stage (16)
 constexpr int kStageBytes = (kFA + kFB) * 1024;
+constexpr int kLoadsPerWave = (kFA + kFB) / 4;
 constexpr int kGroupM = 4;                 // tile rows per raster group
+static_assert(kKS == 2, "the main loop is written for two substeps per stage");
+static_assert(kLoadsPerWave == 8, "vmcnt immediates below assume 8 DMA loads per wave per stage");
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -393,7 +400,7 @@ struct GemmArgs {
     int tiles_m, tiles_n, nmod;
     int64_t m_pad;
     // epilogues
-    uint8_t *planes;         // EPI_MOD: [nmod][n_pad][m_pad]
+    int8_t *planes;          // EPI_MOD: [nmod][n_pad][m_pad], symmetric residues
     int32_t *raw;            // EPI_RAW: [nmod][n_pad][m_pad]
     int32_t *rowmax;         // EPI_BOUND
     int32_t *colmax;
@@ -418,18 +425,19 @@ __device__ __forceinline__ void decode_block(int bid, int total, int tiles_m, in
     tn = in / gsz;
 }
 
-__device__ __forceinline__ int mod_u8(int q, double p, double pinv) {
-    // |q| < 2^31: rint(q/p) is the nearest integer for odd p >= 173 (no ties)
-    // and exact for p = 256; r in [-(p-1)/2, (p-1)/2] (or [-128,128]) -> [0, p).
-    double y = (double)q;
-    int r = (int)fma(-p, rint(y * pinv), y);
-    return r < 0 ? r + (int)p : r;
+// Symmetric residue of an exact int32 product modulo p: |q| < 2^31, so
+// rint(q/p) is the nearest integer for odd p >= 173 (no ties) and exact for
+// p = 256; r lies in [-(p-1)/2, (p-1)/2] (or [-128, 128], stored as a byte,
+// where 128 and -128 are the same residue).
+__device__ __forceinline__ int smod(int q, double p, double pinv) {
+    const double y = (double)q;
+    return (int)fma(-p, rint(y * pinv), y);
 }
 
 template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(GemmArgs ga,
                                                                                          ModConsts mc) {
-    __shared__ __attribute__((aligned(1024))) int8_t lds[2][kStageBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * kStageBytes];
 
     int l, tm, tn;
     decode_block(blockIdx.x, gridDim.x, ga.tiles_m, ga.tiles_n, l, tm, tn);
@@ -447,49 +455,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int nk = (int)(ga.kb / kKS);
 
-    // Each wave copies 8 of the 32 fragment blocks of a stage.
-    auto load_stage = [&](int ks, int buf) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int fbi = wave * 8 + q;
-            const int8_t *src;
-            if (fbi < kFA) {
-                const int rb = fbi / kKS, kk = fbi % kKS;
-                src = gA + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
-            } else {
-                const int f2 = fbi - kFA;
-                const int rb = f2 / kKS, kk = f2 % kKS;
-                src = gB + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
-            }
-            __builtin_amdgcn_global_load_lds(src, LDS_PTR(&lds[buf][fbi * 1024]), 16, 0, 0);
+    // Each wave copies 8 of the 32 fragment blocks of a stage. Past the last
+    // stage the copy is still issued (from the last stage, into the ring slot
+    // that is never read again) so that the main loop has no branch and the
+    // counter waits stay constant.
+    auto dma = [&](int ks_slot, int q) {
+        const int ks = ks_slot < nk ? ks_slot : nk - 1;
+        int8_t *dst = lds + (ks_slot % kNST) * kStageBytes;
+        const int fbi = wave * kLoadsPerWave + q;
+        const int8_t *src;
+        if (fbi < kFA) {
+            const int rb = fbi / kKS, kk = fbi % kKS;
+            src = gA + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
+        } else {
+            const int f2 = fbi - kFA;
+            const int rb = f2 / kKS, kk = f2 % kKS;
+            src = gB + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
         }
+        __builtin_amdgcn_global_load_lds(src, LDS_PTR(dst + fbi * 1024), 16, 0, 0);
+    };
+    // fragment q of a substep: q < 4 -> A tile q, else B tile q - 4
+    auto frag_ptr = [&](const int8_t *stage, int s, int q) {
+        return q < 4 ? stage + ((wm * 4 + q) * kKS + s) * 1024 + lane * 16
+                     : stage + kFA * 1024 + ((wn * 4 + (q - 4)) * kKS + s) * 1024 + lane * 16;
     };
 
-    load_stage(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // The block barriers below are plain s_barrier with explicit counter waits:
+    // __syncthreads() would also drain every in-flight DMA stage.
+#pragma unroll
+    for (int st = 0; st < kNST - 1; ++st)
+#pragma unroll
+        for (int q = 0; q < kLoadsPerWave; ++q) dma(st, q);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");  // kNST-2 stages stay in flight
 
+    v4i f0[8], f1[8];  // fragments of the current / next substep: A tiles 0..3, B tiles 0..3
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f0[q] = *(const v4i *)frag_ptr(lds, 0, q);
+
+    // One substep: 16 MFMA slots; slot q also issues fragment read q (q < 8)
+    // of the next substep and, in the first substep of a stage, DMA copy q.
+    // sched_barrier keeps this exact order.
     for (int ks = 0; ks < nk; ++ks) {
-        const int buf = ks & 1;
-        if (ks + 1 < nk) load_stage(ks + 1, buf ^ 1);
-        const int8_t *sA = &lds[buf][0];
-        const int8_t *sB = &lds[buf][kFA * 1024];
+        const int8_t *cur = lds + (ks % kNST) * kStageBytes;
+        const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
 #pragma unroll
-        for (int s = 0; s < kKS; ++s) {
-            v4i a[4], b[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *(const v4i *)(sA + ((wm * 4 + i) * kKS + s) * 1024 + lane * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = *(const v4i *)(sB + ((wn * 4 + j) * kKS + s) * 1024 + lane * 16);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 16; ++q) {
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[q >> 2], f0[4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 8) {
+                f1[q] = *(const v4i *)frag_ptr(cur, 1, q);
+                dma(ks + kNST - 1, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+        // end of stage: the next stage must have landed and every wave must be
+        // done reading this buffer before anyone refills it
+        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // substep 1; reads fetch substep 0 of the next stage (on the last stage
+        // a stale but valid buffer whose values are never used)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1[q >> 2], f1[4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 8) f0[q] = *(const v4i *)frag_ptr(nxt, 0, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
 
     // Accumulator layout of a 32 x 32 MFMA tile: lane L, register v holds
     // row 8*(v/4) + 4*(L/32) + v%4, column L%32.
@@ -497,7 +529,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int col_base = tn * kTileN + wn * 128 + (lane & 31);
     if (EPI == EPI_MOD) {
         const double p = mc.p[l], pinv = mc.pinv[l];
-        uint8_t *plane = ga.planes + (int64_t)l * ga.plane_elems;
+        int8_t *plane = ga.planes + (int64_t)l * ga.plane_elems;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -506,8 +538,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int row = row_base + 32 * i + 8 * g;
-                    uint32_t w = pack4(mod_u8(acc[i][j][4 * g + 0], p, pinv), mod_u8(acc[i][j][4 * g + 1], p, pinv),
-                                       mod_u8(acc[i][j][4 * g + 2], p, pinv), mod_u8(acc[i][j][4 * g + 3], p, pinv));
+                    uint32_t w = pack4(smod(acc[i][j][4 * g + 0], p, pinv), smod(acc[i][j][4 * g + 1], p, pinv),
+                                       smod(acc[i][j][4 * g + 2], p, pinv), smod(acc[i][j][4 * g + 3], p, pinv));
                     *(uint32_t *)(plane + col * ga.m_pad + row) = w;
                 }
             }
@@ -559,9 +591,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // ---------------------------------------------------------------------------
 // Steps 4 + 5: CRT in exact 40-bit pieces, symmetric lift, round, unscale
 // ---------------------------------------------------------------------------
-// S = sum_l c_l W_l is kept as four doubles S_t (S = sum_t S_t 2^(40 t)); every
-// term c_l W_l,t < 2^48 and the sums stay below 2^52.4, so they are exact in
-// any order. q = round(S / P) comes from a double estimate; X_t = S_t - q P_t
+// S = sum_l c_l W_l (c_l the symmetric residues, |c_l| <= 128) is kept as four
+// doubles S_t (S = sum_t S_t 2^(40 t)); every term |c_l W_l,t| < 2^47 and the
+// sums stay below 2^51.4 in magnitude, so they are exact in any order. q = round(S / P) comes from a double estimate; X_t = S_t - q P_t
 // is again exact, carries are propagated, and the rare estimate that lands a
 // hair outside (-P/2, P/2] is corrected on the exact pieces. The integer X is
 // finally rounded to nearest-even from its 160-bit image, so C equals
@@ -658,7 +690,7 @@ __device__ double crt_finish(double S[4], int ei, int fj, const CrtConsts &cc) {
 }
 
 // One thread per 4 consecutive rows of one column.
-__global__ __launch_bounds__(256) void k_crt(const uint8_t *__restrict__ planes, int64_t plane_elems,
+__global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, int64_t plane_elems,
                                              int64_t m_pad, int64_t m, int64_t n, const int32_t *__restrict__ e,
                                              const int32_t *__restrict__ f, CrtConsts cc, double *__restrict__ C,
                                              int64_t ldc) {
@@ -670,13 +702,13 @@ __global__ __launch_bounds__(256) void k_crt(const uint8_t *__restrict__ planes,
     for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int t = 0; t < 4; ++t) S[u][t] = 0.0;
-    const uint8_t *src = planes + j * m_pad + i0;
+    const int8_t *src = planes + j * m_pad + i0;
     for (int l = 0; l < cc.n; ++l) {
-        const uint32_t w = *(const uint32_t *)(src + (int64_t)l * plane_elems);
+        const int32_t w = *(const int32_t *)(src + (int64_t)l * plane_elems);
         const double w0 = cc.w[l][0], w1 = cc.w[l][1], w2 = cc.w[l][2], w3 = cc.w[l][3];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const double c = (double)((w >> (8 * u)) & 0xffu);
+            const double c = (double)((w << (24 - 8 * u)) >> 24);  // signed byte u
             S[u][0] = fma(c, w0, S[u][0]);
             S[u][1] = fma(c, w1, S[u][1]);
             S[u][2] = fma(c, w2, S[u][2]);
@@ -719,13 +751,27 @@ __global__ void k_unpack(const int8_t *packed, int64_t rows, int64_t k, int64_t 
     }
 }
 
-template <typename T>
-__global__ void k_copy_planes(const T *planes, int64_t m, int64_t m_pad, int64_t plane_elems, int64_t n,
-                              T *out) {
+__global__ void k_copy_planes_i32(const int32_t *planes, int64_t m, int64_t m_pad, int64_t plane_elems, int64_t n,
+                                  int32_t *out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t l = blockIdx.z;
     if (i >= m) return;
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) out[(l * n + j) * m + i] = planes[l * plane_elems + j * m_pad + i];
+}
+
+// symmetric residues -> [0, p)
+__global__ void k_copy_planes_red(const int8_t *planes, int64_t m, int64_t m_pad, int64_t plane_elems, int64_t n,
+                                  ModConsts mc, uint8_t *out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t l = blockIdx.z;
+    if (i >= m) return;
+    const int p = (int)mc.p[l];
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        int v = planes[l * plane_elems + j * m_pad + i];
+        if (p == 256) v &= 0xff;
+        else if (v < 0) v += p;
+        out[(l * n + j) * m + i] = (uint8_t)v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -799,7 +845,7 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, const La
     return g;
 }
 
-hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc, uint8_t *planes,
+hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc, int8_t *planes,
                            const Layout &L, hipStream_t s) {
     GemmArgs g = gemm_args(RA, RB, nmod, L);
     g.planes = planes;
@@ -837,7 +883,7 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
     return hipGetLastError();
 }
 
-hipError_t launch_crt(const uint8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s) {
     dim3 grid(nblk((m + 3) / 4, 256), ydim(n));
     hipLaunchKernelGGL(k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
@@ -856,17 +902,17 @@ hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, 
     return hipGetLastError();
 }
 
-hipError_t launch_copy_planes_u8(const uint8_t *planes, int nmod, int64_t m, int64_t n, const Layout &L,
-                                 uint8_t *out, hipStream_t s) {
+hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,
+                                 const Layout &L, uint8_t *out, hipStream_t s) {
     dim3 grid(nblk(m, 256), ydim(n), (unsigned)nmod);
-    hipLaunchKernelGGL(k_copy_planes<uint8_t>, grid, dim3(256), 0, s, planes, m, L.m_pad, L.m_pad * L.n_pad, n, out);
+    hipLaunchKernelGGL(k_copy_planes_red, grid, dim3(256), 0, s, planes, m, L.m_pad, L.m_pad * L.n_pad, n, mc, out);
     return hipGetLastError();
 }
 
 hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
                                   int32_t *out, hipStream_t s) {
     dim3 grid(nblk(m, 256), ydim(n), (unsigned)nmod);
-    hipLaunchKernelGGL(k_copy_planes<int32_t>, grid, dim3(256), 0, s, raw, m, L.m_pad, L.m_pad * L.n_pad, n, out);
+    hipLaunchKernelGGL(k_copy_planes_i32, grid, dim3(256), 0, s, raw, m, L.m_pad, L.m_pad * L.n_pad, n, out);
     return hipGetLastError();
 }
 
