@@ -53,10 +53,11 @@ Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool deb
     L.n_pad = round_up(n > 0 ? n : 1, kTileN);
     L.k_pad = round_up(k > 0 ? k : 1, kKPad);
     L.kb = L.k_pad / 32;
-    // k-chunks of the row-norm pass: enough blocks to fill 256 CUs several times
-    const int64_t rowblocks = (m + 255) / 256 > 0 ? (m + 255) / 256 : 1;
-    int64_t want = (2048 + rowblocks - 1) / rowblocks;
-    int64_t maxc = (k + 15) / 16 > 0 ? (k + 15) / 16 : 1;
+    // k-chunks of the row-norm pass (blocks of 64 rows): about 1024 blocks,
+    // each thread still streaming at least 32 columns
+    const int64_t rowblocks = (m + 63) / 64 > 0 ? (m + 63) / 64 : 1;
+    int64_t want = (1024 + rowblocks - 1) / rowblocks;
+    int64_t maxc = (k + 127) / 128 > 0 ? (k + 127) / 128 : 1;
     if (want > maxc) want = maxc;
     if (want > 65535) want = 65535;
     if (want < 1) want = 1;

@@ -71,41 +71,59 @@ __device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
     return (int)floor(z) - h;
 }
 
-// Rows of column-major A: thread = row, block column = k-chunk; partial
+// Rows of column-major A. Block = 64 rows x 4 k-lanes over one k-chunk: a
+// wavefront reads 64 consecutive rows of one column (512 contiguous bytes),
+// each thread accumulates every 4th column of its chunk, and the 4 lanes of a
+// row are merged in a fixed order through LDS. Output: one partial
 // (s, g, nonfinite) per (chunk, row).
 __global__ __launch_bounds__(256) void k_row_norms(const double *__restrict__ A, int64_t m, int64_t k,
                                                    int64_t lda, int64_t kchunk, double *__restrict__ ps,
                                                    int *__restrict__ pg, int *__restrict__ pbad) {
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= m) return;
-    int64_t h0 = (int64_t)blockIdx.y * kchunk;
-    int64_t h1 = h0 + kchunk < k ? h0 + kchunk : k;
+    __shared__ double sh_s[4][64];
+    __shared__ int sh_g[4][64];
+    __shared__ int sh_b[4][64];
+    const int r = threadIdx.x & 63, kl = threadIdx.x >> 6;
+    const int64_t i = (int64_t)blockIdx.x * 64 + r;
+    const int64_t h0 = (int64_t)blockIdx.y * kchunk;
+    const int64_t h1 = h0 + kchunk < k ? h0 + kchunk : k;
     double s = 0.0;
     int g = kExpEmpty;
     int bad = 0;
-    const double *a = A + i + h0 * lda;
-    int64_t h = h0;
-    for (; h + 8 <= h1; h += 8) {
-        double v[8];
+    if (i < m) {
+        const double *a = A + i;
+        int64_t h = h0 + kl;
+        for (; h + 28 < h1; h += 32) {
+            double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = a[u * lda];
-        a += 8 * lda;
+            for (int u = 0; u < 8; ++u) v[u] = a[(h + 4 * u) * lda];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            double x = fabs(v[u]);
+            for (int u = 0; u < 8; ++u) {
+                double x = fabs(v[u]);
+                if (!(x <= DBL_MAX)) bad = 1;
+                else ssq_add(s, g, x);
+            }
+        }
+        for (; h < h1; h += 4) {
+            double x = fabs(a[h * lda]);
             if (!(x <= DBL_MAX)) bad = 1;
             else ssq_add(s, g, x);
         }
     }
-    for (; h < h1; ++h, a += lda) {
-        double x = fabs(*a);
-        if (!(x <= DBL_MAX)) bad = 1;
-        else ssq_add(s, g, x);
+    sh_s[kl][r] = s;
+    sh_g[kl][r] = g;
+    sh_b[kl][r] = bad;
+    __syncthreads();
+    if (kl == 0 && i < m) {
+#pragma unroll
+        for (int q = 1; q < 4; ++q) {
+            ssq_merge(s, g, sh_s[q][r], sh_g[q][r]);
+            bad |= sh_b[q][r];
+        }
+        const int64_t o = (int64_t)blockIdx.y * m + i;
+        ps[o] = s;
+        pg[o] = g;
+        pbad[o] = bad;
     }
-    int64_t o = (int64_t)blockIdx.y * m + i;
-    ps[o] = s;
-    pg[o] = g;
-    pbad[o] = bad;
 }
 
 // Combine the chunks of each row in ascending order; e = fast exponent,
@@ -162,12 +180,12 @@ __global__ __launch_bounds__(256) void k_col_exponents(const double *__restrict_
     int g = kExpEmpty;
     int bad = 0;
     int64_t h = lane;
-    for (; h + 3 * 64 < k; h += 4 * 64) {
-        double v[4];
+    for (; h + 7 * 64 < k; h += 8 * 64) {
+        double v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = col[h + 64 * u];
+        for (int u = 0; u < 8; ++u) v[u] = col[h + 64 * u];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             double x = fabs(v[u]);
             if (!(x <= DBL_MAX)) bad = 1;
             else ssq_add(s, g, x);
@@ -615,112 +633,131 @@ __device__ __forceinline__ int sign4(const double x[4]) {
     return (x[2] != 0.0 || x[1] != 0.0 || x[0] != 0.0) ? 1 : 0;
 }
 
-__device__ double limbs_to_double_rn(const double x[4], int scale_down) {
-    // x normalized and non-negative: x[0..2] in [0, 2^40), x[3] in [0, 2^36)
-    const uint64_t L0 = (uint64_t)x[0], L1 = (uint64_t)x[1], L2 = (uint64_t)x[2], L3 = (uint64_t)x[3];
+// Integer value of a double holding an integer in [0, 2^52): adding 2^52
+// puts it in the significand field.
+__device__ __forceinline__ uint64_t small_int_bits(double x) {
+    return (uint64_t)__double_as_longlong(x + 0x1p52) & ((1ull << 52) - 1);
+}
+
+// RN(x) * 2^-scale_down for a normalized non-negative piece vector
+// (x[0..2] in [0, 2^40), x[3] in [0, 2^36)), rounded to nearest-even from the
+// exact 160-bit integer.
+__device__ __forceinline__ double limbs_to_double_rn(const double x[4], int scale_down) {
+    const uint64_t L0 = small_int_bits(x[0]), L1 = small_int_bits(x[1]), L2 = small_int_bits(x[2]),
+                   L3 = small_int_bits(x[3]);
     const uint64_t w0 = L0 | (L1 << 40);
     const uint64_t w1 = (L1 >> 24) | (L2 << 16) | (L3 << 56);
     const uint64_t w2 = L3 >> 8;
-    uint64_t hi;
-    bool sticky;
-    int scale;  // value = hi * 2^scale + rest, 0 <= rest < 2^scale
+    // value = hi * 2^scale + rest, hi normalized to bit 63, sticky = (rest != 0)
+    uint64_t top, nxt, low;
+    int scale;
     if (w2) {
-        const int lz = __clzll(w2);
-        hi = lz ? (w2 << lz) | (w1 >> (64 - lz)) : w2;
-        sticky = ((lz ? (w1 << lz) : w1) | w0) != 0;
-        scale = 128 - lz;
+        top = w2; nxt = w1; low = w0; scale = 128;
     } else if (w1) {
-        const int lz = __clzll(w1);
-        hi = lz ? (w1 << lz) | (w0 >> (64 - lz)) : w1;
-        sticky = (lz ? (w0 << lz) : w0) != 0;
-        scale = 64 - lz;
-    } else if (w0) {
-        const int lz = __clzll(w0);
-        hi = w0 << lz;
-        sticky = false;
-        scale = -lz;
+        top = w1; nxt = w0; low = 0; scale = 64;
     } else {
-        return 0.0;
+        top = w0; nxt = 0; low = 0; scale = 0;
     }
+    if (top == 0) return 0.0;
+    const int lz = __clzll(top);
+    const uint64_t hi = lz ? (top << lz) | (nxt >> (64 - lz)) : top;
+    const bool sticky = ((lz ? (nxt << lz) : nxt) | low) != 0;
     uint64_t mant = hi >> 11;
     const uint64_t rb = hi & 0x7ff;
-    if (rb > 0x400 || (rb == 0x400 && (sticky || (mant & 1)))) mant += 1;
-    return ldexp((double)mant, scale + 11 - scale_down);
+    mant += (rb > 0x400 || (rb == 0x400 && (sticky || (mant & 1)))) ? 1 : 0;
+    return ldexp((double)mant, scale - lz + 11 - scale_down);
 }
 
-__device__ double crt_finish(double S[4], int ei, int fj, const CrtConsts &cc) {
-    if (ei == kExpNonfinite || fj == kExpNonfinite) return __builtin_nan("");
-    // S / P estimate (relative error ~2^-51; S/P < 2^13)
+// Exact repair of an estimated quotient: bring X into (-P/2, P/2].
+__device__ __forceinline__ void crt_range_fix(double x[4], const CrtConsts &cc) {
+    double z[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[t] = x[t] - cc.H[t];
+    normalize4(z);
+    if (sign4(z) > 0) {  // X > P/2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] -= cc.P[t];
+        normalize4(x);
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[t] = x[t] + cc.H[t];
+    normalize4(z);
+    if (sign4(z) <= 0) {  // X <= -P/2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] += cc.P[t];
+        normalize4(x);
+    }
+}
+
+__device__ __forceinline__ double crt_finish(const double S[4], int ei, int fj, const CrtConsts &cc) {
+    // S / P estimate (relative error ~2^-51; |S/P| < 2^12)
     const double s120 = fma(S[0], 0x1p-120, fma(S[1], 0x1p-80, fma(S[2], kTwoM40, S[3])));
     const double quo = s120 * cc.pinv120;
     const double q = rint(quo);
+    const double d = quo - q;  // ~ X / P
+    // Work on |X| directly: the sign of X is that of d unless |X| is below
+    // 2^-30 P, which the exact check after normalizing catches.
+    double sg = d < 0.0 ? -1.0 : 1.0;
     double x[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) x[t] = fma(-q, cc.P[t], S[t]);
+    for (int t = 0; t < 4; ++t) x[t] = sg * fma(-q, cc.P[t], S[t]);
     normalize4(x);
-    if (fabs(quo - q) > 0.5 - 0x1p-30) {
-        // exact check of -P/2 < X <= P/2 on the pieces
-        double z[4];
+    if (fabs(d) > 0.5 - 0x1p-30) {  // near +-P/2: settle the wrap exactly (never on valid scalings)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) z[t] = x[t] - cc.H[t];
-        normalize4(z);
-        if (sign4(z) > 0) {  // X > P/2
+        for (int t = 0; t < 4; ++t) x[t] *= sg;
+        crt_range_fix(x, cc);
+        sg = sign4(x) < 0 ? -1.0 : 1.0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) x[t] -= cc.P[t];
-            normalize4(x);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) z[t] = x[t] + cc.H[t];
-            normalize4(z);
-            if (sign4(z) <= 0) {  // X <= -P/2
-#pragma unroll
-                for (int t = 0; t < 4; ++t) x[t] += cc.P[t];
-                normalize4(x);
-            }
-        }
+        for (int t = 0; t < 4; ++t) x[t] *= sg;
+        normalize4(x);
     }
-    const bool neg = x[3] < 0.0;
-    if (neg) {
+    if (x[3] < 0.0) {  // sign predicted wrongly (|X| tiny)
 #pragma unroll
         for (int t = 0; t < 4; ++t) x[t] = -x[t];
         normalize4(x);
+        sg = -sg;
     }
     const double mag = limbs_to_double_rn(x, ei + fj);
-    return neg ? -mag : mag;
+    return (ei == kExpNonfinite || fj == kExpNonfinite) ? __builtin_nan("") : sg * mag;
 }
 
-// One thread per 4 consecutive rows of one column.
+// One thread per 4 consecutive rows of one column. The loop over the moduli is
+// kept rolled (one plane load per trip): on MI355X this overlaps the plane
+// traffic with the arithmetic better than hoisting all loads.
+constexpr int kCrtRows = 4;
 __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, int64_t plane_elems,
                                              int64_t m_pad, int64_t m, int64_t n, const int32_t *__restrict__ e,
                                              const int32_t *__restrict__ f, CrtConsts cc, double *__restrict__ C,
                                              int64_t ldc) {
-    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kCrtRows;
     if (i0 >= m) return;
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
-    double S[4][4];
+        const int8_t *src = planes + j * m_pad + i0;
+        double S[kCrtRows][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < kCrtRows; ++u)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) S[u][t] = 0.0;
-    const int8_t *src = planes + j * m_pad + i0;
-    for (int l = 0; l < cc.n; ++l) {
-        const int32_t w = *(const int32_t *)(src + (int64_t)l * plane_elems);
-        const double w0 = cc.w[l][0], w1 = cc.w[l][1], w2 = cc.w[l][2], w3 = cc.w[l][3];
+            for (int t = 0; t < 4; ++t) S[u][t] = 0.0;
+#pragma unroll 1
+        for (int l = 0; l < cc.n; ++l) {
+            const int32_t w = *(const int32_t *)(src + (int64_t)l * plane_elems);
+            const double w0 = cc.w[l][0], w1 = cc.w[l][1], w2 = cc.w[l][2], w3 = cc.w[l][3];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const double c = (double)((w << (24 - 8 * u)) >> 24);  // signed byte u
-            S[u][0] = fma(c, w0, S[u][0]);
-            S[u][1] = fma(c, w1, S[u][1]);
-            S[u][2] = fma(c, w2, S[u][2]);
-            S[u][3] = fma(c, w3, S[u][3]);
+            for (int u = 0; u < kCrtRows; ++u) {
+                const double c = (double)((w << (24 - 8 * u)) >> 24);  // signed byte u
+                S[u][0] = fma(c, w0, S[u][0]);
+                S[u][1] = fma(c, w1, S[u][1]);
+                S[u][2] = fma(c, w2, S[u][2]);
+                S[u][3] = fma(c, w3, S[u][3]);
+            }
         }
-    }
-    const int fj = f[j];
+        const int fj = f[j];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int64_t i = i0 + u;
-        if (i < m) C[i + j * ldc] = crt_finish(S[u], e[i], fj, cc);
-    }
+        for (int u = 0; u < kCrtRows; ++u) {
+            const int64_t i = i0 + u;
+            if (i < m) C[i + j * ldc] = crt_finish(S[u], e[i], fj, cc);
+        }
     }
 }
 
@@ -782,7 +819,7 @@ static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (
 
 hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L, char *ws,
                             hipStream_t s) {
-    dim3 grid(nblk(m, 256), (unsigned)L.nchunks);
+    dim3 grid(nblk(m, 64), (unsigned)L.nchunks);
     hipLaunchKernelGGL(k_row_norms, grid, dim3(256), 0, s, A, m, k, lda, L.kchunk, (double *)(ws + L.part_s),
                        (int *)(ws + L.part_g), (int *)(ws + L.part_bad));
     return hipGetLastError();
@@ -885,7 +922,7 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
 
 hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s) {
-    dim3 grid(nblk((m + 3) / 4, 256), ydim(n));
+    dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
     hipLaunchKernelGGL(k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     return hipGetLastError();
 }
