@@ -46,8 +46,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
     Problemstellung) is read as: bound |A| and |B| from above by 6-bit
     integers on the row/column maxima, form their product with one extra
     integer GEMM, and choose each row's exponent from the largest entry of its
-    row of that product (and likewise for columns). Parity of that mode is
-    pinned only by its invariants.
+    row of that product (and likewise for columns). PARITY UNPINNED as to the
+    exact rule: the pages print no algorithm or value for it; only its
+    invariants are pinned (the range condition holds exactly, the scale law,
+    the bound operands really bound |A| and |B|).
 """
 from __future__ import annotations
 
