@@ -260,31 +260,42 @@ template <bool KCONTIG>
 __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const double *__restrict__ X,
                                                 int64_t rows, int64_t kdim, int64_t ld, int64_t r0,
                                                 int64_t h0) {
+    // All 16 loads of a thread are issued before any LDS write; out-of-range
+    // elements read a valid address and are replaced by zero.
     const int t = threadIdx.x;
+    double v[16];
     if (!KCONTIG) {  // element (r, h) at X[r + h*ld]: rows contiguous
         const int rr = t & 31, hh = t >> 5;
         const int64_t r = r0 + rr;
+        const bool rok = r < rows;
+        const int64_t rc = rok ? r : 0;
 #pragma unroll
         for (int it = 0; it < 16; ++it) {
-            const int hk = hh + 8 * it;
-            const int64_t h = h0 + hk;
-            tile[rr][hk] = (r < rows && h < kdim) ? X[r + h * ld] : 0.0;
+            const int64_t h = h0 + hh + 8 * it;
+            const bool ok = rok && h < kdim;
+            const double x = X[rc + (ok ? h : 0) * ld];
+            v[it] = ok ? x : 0.0;
         }
+#pragma unroll
+        for (int it = 0; it < 16; ++it) tile[rr][hh + 8 * it] = v[it];
     } else {  // element (r, h) at X[h + r*ld]: K contiguous
         const int hh = (t & 63) * 2, rq = t >> 6;
         const int64_t h = h0 + hh;
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
+            const int64_t r = r0 + rq + 4 * it;
+            const bool rok = r < rows;
+            const bool ok0 = rok && h < kdim, ok1 = rok && h + 1 < kdim;
+            const double *row = X + (rok ? r : 0) * ld;
+            const double x0 = row[ok0 ? h : 0], x1 = row[ok1 ? h + 1 : 0];
+            v[2 * it] = ok0 ? x0 : 0.0;
+            v[2 * it + 1] = ok1 ? x1 : 0.0;
+        }
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
             const int rr = rq + 4 * it;
-            const int64_t r = r0 + rr;
-            double v0 = 0.0, v1 = 0.0;
-            if (r < rows) {
-                const double *src = X + r * ld + h;
-                if (h < kdim) v0 = src[0];
-                if (h + 1 < kdim) v1 = src[1];
-            }
-            tile[rr][hh] = v0;
-            tile[rr][hh + 1] = v1;
+            tile[rr][hh] = v[2 * it];
+            tile[rr][hh + 1] = v[2 * it + 1];
         }
     }
 }
