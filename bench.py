@@ -39,6 +39,25 @@ def parse():
     return p.parse_args()
 
 
+def gemm_traffic_bytes():
+    """HBM bytes per GEMM launch from the committed counter runs, or None.
+
+    The figure is used only while the GEMM source still hashes to the one the
+    counters were taken on.
+    """
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_gemm_spread1.0_4096_n16_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "kernels.hip")).read()
+    sec = src[src.index("// Step 3: INT8 GEMM"):src.index("// Steps 4 + 5")]
+    common = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "common.h")).read()
+    if hashlib.sha256((sec + common).encode()).hexdigest() != rec["gemm_source_sha256"]:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -158,8 +177,9 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     int8_ops = N * flops  # one INT8 GEMM per modulus, all in one launch
     gemm_tops = int8_ops / (phase_avg["gemm"] * 1e-3) / 1e12
+    traffic = gemm_traffic_bytes() if args.config == "spread1.0_4096_n16" and args.mode == "fast" else None
     roofline = dict(bound="mfma", achieved=round(gemm_tops, 2), peak=INT8_PEAK_TOPS, unit="TFLOP/s",
-                    frac=round(gemm_tops / INT8_PEAK_TOPS, 4), traffic=None,
+                    frac=round(gemm_tops / INT8_PEAK_TOPS, 4), traffic=traffic,
                     kernel="k_gemm<EPI_MOD>", ops_per_launch=int8_ops, dtype="int8")
 
     C = dC.cpu().numpy().T  # C of the last step
