@@ -85,7 +85,7 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
     omp_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     m, k = A.shape
     n = B.shape[1]
-    rows = rows_wanted or max(8, min(m, int(1536 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
+    rows = rows_wanted or max(8, min(m, int(3072 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
     rows = min(rows, m)
     log(f"cpu_baseline: oracle on {rows} rows x {n} columns, k={k}, N={N}, {mode}")
     t0 = time.perf_counter()

@@ -214,3 +214,48 @@ def test_config_scale_sweep_2048_n14():
             assert np.array_equal(g["e"], base["e"] - s)
             assert_bitwise_equal(g["C"], np.ldexp(base["C"], s), f"scale 2^{s}")
         _sampled_exact_check(A, B, base["C"], base["e"].tolist(), base["f"].tolist(), rows, cols)
+
+
+def test_config_spread1_16384_n18():
+    # 16384^3, N = 18 (2 GiB per operand; |x| reaches 2^69.7, beyond int64):
+    # exponents of sampled rows/columns, C bit-exact on sampled entries, and the
+    # accuracy gate on sampled rows.
+    A, B = W.make("spread1.0_16384_n18")
+    m, k = A.shape
+    n = B.shape[1]
+    N = 18
+    dA = device_colmajor(A)
+    dB = device_colmajor(B)
+    dC = torch.empty((n, m), dtype=torch.float64, device="cuda")
+    wbytes = oz.ozaki2_debug_workspace_size(m, n, k, N, 0)
+    ws = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
+    e = torch.empty(m, dtype=torch.int32, device="cuda")
+    f = torch.empty(n, dtype=torch.int32, device="cuda")
+    st = oz.ozaki2_dgemm_debug(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, 0, ws.data_ptr(),
+                               wbytes, e.data_ptr(), f.data_ptr(), None, None, None, None, stream_handle())
+    assert st == 0
+    torch.cuda.synchronize()
+    del ws, dA, dB
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(m, 6, replace=False)).tolist()
+    cols = np.sort(rng.choice(n, 6, replace=False)).tolist()
+    C = dC[cols, :][:, rows].cpu().numpy().T  # C[rows][:, cols]
+    Crows = dC[:, rows[:3]].cpu().numpy().T   # full rows for the accuracy gate
+    ge = e.cpu().numpy().tolist()
+    gf = f.cpu().numpy().tolist()
+    Pp = O.scaling_constant(math.prod(O.choose_moduli(N)))
+    oe = O.fast_exponents_rows(A[rows], Pp)
+    of = O.fast_exponents_rows(B[:, cols].T, Pp)
+    assert sum(a != b for a, b in zip(oe, [ge[i] for i in rows])) == 0
+    assert sum(a != b for a, b in zip(of, [gf[j] for j in cols])) == 0
+    Ai = O.scaled_integers(A[rows], [ge[i] for i in rows])
+    Bi = O.scaled_integers(B[:, cols].T, [gf[j] for j in cols])
+    Y = Ai.dot(Bi.T)
+    P = math.prod(O.choose_moduli(N))
+    assert np.all(2 * np.abs(Y) <= P - 1)
+    ref = O.unscale(Y, [ge[i] for i in rows], [gf[j] for j in cols])
+    assert_bitwise_equal(C, ref, "sampled C at 16384^3")
+    hi, lo = O.dd_gemm(A[rows[:3]], B)
+    err = O.error_metrics(Crows, hi, lo, A[rows[:3]], B)
+    print("16384^3 N=18:", err)
+    assert err["E_cw"] <= 1e-14
