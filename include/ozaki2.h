@@ -166,15 +166,18 @@ int ozaki2_crt_weight(int num_moduli, int l, uint32_t *out_le32, int out_limbs);
 const char *ozaki2_status_string(int status);
 
 /*
- * Per-phase timing with HIP events recorded on the caller's stream around
- * each phase of every product call (phases: 0 scaling/exponents, 1 residue
- * split, 2 INT8 GEMMs, 3 CRT + unscale). ozaki2_timing_enable(max_calls)
- * creates the events (0 turns timing off); ozaki2_timing_read synchronises
- * the recorded events, writes the summed milliseconds per phase to
- * HOST ms_out[4] and the number of timed calls to *calls, and clears the
- * record. Returns 0 or OZAKI2_ERR_HIP.
+ * Per-phase timing with HIP events recorded on the caller's stream right
+ * before the first and right after the last kernel of a phase (phases: 0
+ * scaling/exponents, 1 residue split, 2 INT8 GEMMs, 3 CRT + unscale).
+ * ozaki2_timing_enable(max_calls, all_phases) creates events for up to
+ * max_calls product calls (max_calls <= 0 turns timing off); with
+ * all_phases == 0 only phase 2 is timed, which keeps the extra stream time to
+ * two event records per call. ozaki2_timing_read synchronises them, writes the
+ * summed milliseconds per phase to HOST ms_out[4] (0 for untimed phases) and
+ * the number of timed calls to *calls, and clears the record.
+ * Returns 0 or OZAKI2_ERR_HIP.
  */
-int ozaki2_timing_enable(int max_calls);
+int ozaki2_timing_enable(int max_calls, int all_phases);
 int ozaki2_timing_read(double *ms_out, int *calls);
 
 /* Frees the cached workspaces, timing events and tables. */

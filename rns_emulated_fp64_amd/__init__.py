@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_crt_weight.restype = i32
     L.ozaki2_status_string.argtypes = [i32]
     L.ozaki2_status_string.restype = ctypes.c_char_p
-    L.ozaki2_timing_enable.argtypes = [i32]
+    L.ozaki2_timing_enable.argtypes = [i32, i32]
     L.ozaki2_timing_enable.restype = i32
     L.ozaki2_timing_read.argtypes = [p, p]
     L.ozaki2_timing_read.restype = i32
@@ -135,8 +135,8 @@ def status_string(status: int) -> str:
     return lib().ozaki2_status_string(status).decode()
 
 
-def ozaki2_timing_enable(max_calls: int) -> None:
-    st = lib().ozaki2_timing_enable(max_calls)
+def ozaki2_timing_enable(max_calls: int, all_phases: bool = False) -> None:
+    st = lib().ozaki2_timing_enable(max_calls, 1 if all_phases else 0)
     if st:
         raise Ozaki2Error(st, "ozaki2_timing_enable")
 

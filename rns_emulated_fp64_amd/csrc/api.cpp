@@ -95,9 +95,10 @@ Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool deb
 // ---- timing ---------------------------------------------------------------
 struct Timing {
     std::mutex mu;
-    std::vector<hipEvent_t> ev;  // (kNumPhases + 1) per call
+    std::vector<hipEvent_t> ev;  // 2 * kNumPhases per call: start, stop of each phase
     int max_calls = 0;
     int used = 0;
+    bool all_phases = false;  // false: only the GEMM phase is timed
 };
 Timing g_timing;
 
@@ -112,7 +113,7 @@ void timing_free_locked() {
 hipEvent_t *timing_slots() {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     if (g_timing.used >= g_timing.max_calls) return nullptr;
-    return &g_timing.ev[(size_t)(g_timing.used++) * (kNumPhases + 1)];
+    return &g_timing.ev[(size_t)(g_timing.used++) * (2 * kNumPhases)];
 }
 
 // ---- cached workspace per device ------------------------------------------
@@ -138,15 +139,28 @@ struct DebugOut {
 int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb, double *C,
         int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
     const Tables *T = get_tables(nmod);
+    // Timing events (start/stop per phase) are recorded before the first and
+    // after the last kernel of a phase; unless all phases were asked for, only
+    // the GEMM phase is timed (each record costs a few microseconds of stream
+    // time).
     hipEvent_t *ev = timing_slots();
-    if (ev) HIP_TRY(hipEventRecord(ev[0], s));
+    const bool all_phases = g_timing.all_phases;
+    auto ev_of = [&](int phase, bool first, bool last) {
+        Ev e;
+        if (ev && (all_phases || phase == kPhaseGemm)) {
+            if (first) e.start = ev[2 * phase];
+            if (last) e.stop = ev[2 * phase + 1];
+        }
+        return e;
+    };
+    const bool accurate = mode == OZAKI2_ACCURATE;
 
     // Step 1: exponents ([G] Methodik for fast mode; accurate mode bounds the
     // products with one extra INT8 GEMM first).
-    HIP_TRY(launch_row_norms(A, m, k, lda, L, ws, s));
+    HIP_TRY(launch_row_norms(A, m, k, lda, L, ws, s, ev_of(kPhaseScale, true, false)));
     HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
-    HIP_TRY(launch_col_exponents(B, k, n, ldb, T->Pp, L, ws, s));
-    if (mode == OZAKI2_ACCURATE) {
+    HIP_TRY(launch_col_exponents(B, k, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, false, !accurate)));
+    if (accurate) {
         HIP_TRY(launch_quantize(A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
                                 L.m_pad, L, s));
         HIP_TRY(launch_quantize(B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
@@ -155,24 +169,23 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
         HIP_TRY(launch_fill_i32((int32_t *)(ws + L.colmax), L.n_pad, 0, s));
         HIP_TRY(launch_gemm_bound((const int8_t *)(ws + L.abar), (const int8_t *)(ws + L.bbar),
                                   (int32_t *)(ws + L.rowmax), (int32_t *)(ws + L.colmax), L, s));
-        HIP_TRY(launch_accurate_exponents(m, n, T->Pp, L, ws, s));
+        HIP_TRY(launch_accurate_exponents(m, n, T->Pp, L, ws, s, ev_of(kPhaseScale, false, true)));
     }
-    if (ev) HIP_TRY(hipEventRecord(ev[1], s));
 
     // Steps 1 + 2: integerize and split into residues.
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
-    HIP_TRY(launch_split(A, m, k, lda, false, e, T->split, (int8_t *)(ws + L.ra), L.m_pad, L, s));
-    HIP_TRY(launch_split(B, n, k, ldb, true, f, T->split, (int8_t *)(ws + L.rb), L.n_pad, L, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[2], s));
+    HIP_TRY(launch_split(A, m, k, lda, false, e, T->split, (int8_t *)(ws + L.ra), L.m_pad, L, s,
+                         ev_of(kPhaseSplit, true, false)));
+    HIP_TRY(launch_split(B, n, k, ldb, true, f, T->split, (int8_t *)(ws + L.rb), L.n_pad, L, s,
+                         ev_of(kPhaseSplit, false, true)));
 
     // Step 3: one exact INT8 product per modulus, reduced mod p_l.
     HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, T->mod,
-                            (int8_t *)(ws + L.planes), L, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[3], s));
+                            (int8_t *)(ws + L.planes), L, s, ev_of(kPhaseGemm, true, true)));
 
     // Steps 4 + 5: reconstruction and unscaling.
-    HIP_TRY(launch_crt((const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s));
-    if (ev) HIP_TRY(hipEventRecord(ev[4], s));
+    HIP_TRY(launch_crt((const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
+                       ev_of(kPhaseCrt, true, true)));
 
     if (dbg) {
         if (dbg->e) HIP_TRY(hipMemcpyAsync(dbg->e, e, 4 * (size_t)m, hipMemcpyDeviceToDevice, s));
@@ -314,11 +327,12 @@ const char *ozaki2_status_string(int status) {
     return "unknown status";
 }
 
-int ozaki2_timing_enable(int max_calls) {
+int ozaki2_timing_enable(int max_calls, int all_phases) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     timing_free_locked();
+    g_timing.all_phases = all_phases != 0;
     if (max_calls <= 0) return OZAKI2_SUCCESS;
-    g_timing.ev.resize((size_t)max_calls * (kNumPhases + 1));
+    g_timing.ev.resize((size_t)max_calls * (2 * kNumPhases));
     for (hipEvent_t &e : g_timing.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
@@ -334,11 +348,13 @@ int ozaki2_timing_read(double *ms_out, int *calls) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     double acc[kNumPhases] = {0, 0, 0, 0};
     for (int c = 0; c < g_timing.used; ++c) {
-        hipEvent_t *ev = &g_timing.ev[(size_t)c * (kNumPhases + 1)];
-        if (hipEventSynchronize(ev[kNumPhases]) != hipSuccess) return OZAKI2_ERR_HIP;
+        hipEvent_t *ev = &g_timing.ev[(size_t)c * (2 * kNumPhases)];
+        if (hipEventSynchronize(ev[2 * kPhaseGemm + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
         for (int p = 0; p < kNumPhases; ++p) {
+            if (!g_timing.all_phases && p != kPhaseGemm) continue;
+            if (g_timing.all_phases && hipEventSynchronize(ev[2 * p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
             float ms = 0.f;
-            if (hipEventElapsedTime(&ms, ev[p], ev[p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
+            if (hipEventElapsedTime(&ms, ev[2 * p], ev[2 * p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
             acc[p] += ms;
         }
     }

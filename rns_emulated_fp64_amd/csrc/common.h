@@ -68,29 +68,36 @@ struct Layout {
 
 enum Phase { kPhaseScale = 0, kPhaseSplit = 1, kPhaseGemm = 2, kPhaseCrt = 3, kNumPhases = 4 };
 
+// Optional timing events recorded on the stream right before (start) and
+// right after (stop) one kernel launch.
+struct Ev {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
 hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L,
-                            char *ws, hipStream_t s);
+                            char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s);
 hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp,
-                                const Layout &L, char *ws, hipStream_t s);
+                                const Layout &L, char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                         const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad,
-                        const Layout &L, hipStream_t s);
+                        const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                            const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
                            hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc,
-                           int8_t *planes, const Layout &L, hipStream_t s);
+                           int8_t *planes, const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw,
                            const Layout &L, hipStream_t s);
 hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
                              const Layout &L, hipStream_t s);
 hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws,
-                                     hipStream_t s);
+                                     hipStream_t s, Ev ev = {});
 hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
-                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s);
+                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
 hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);

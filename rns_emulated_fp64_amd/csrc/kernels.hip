@@ -21,6 +21,14 @@
 
 namespace oz2 {
 
+// Launch with optional timing events recorded right before / after it.
+#define OZ2_LAUNCH(ev, kern, grid, block, shm, stream, ...)              \
+    do {                                                               \
+        if ((ev).start) (void)hipEventRecord((ev).start, stream);      \
+        hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__); \
+        if ((ev).stop) (void)hipEventRecord((ev).stop, stream);        \
+    } while (0)
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
@@ -470,11 +478,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     int l, tm, tn;
     decode_block(blockIdx.x, gridDim.x, ga.tiles_m, ga.tiles_n, l, tm, tn);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // wave index made explicitly wave-uniform so that all DMA addressing below
+    // stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
-
-    const int8_t *gA = ga.RA + (int64_t)l * ga.planeA + (int64_t)tm * (kTileM / 32) * ga.kb * 1024 + lane * 16;
-    const int8_t *gB = ga.RB + (int64_t)l * ga.planeB + (int64_t)tn * (kTileN / 32) * ga.kb * 1024 + lane * 16;
 
     v16i acc[4][4];
 #pragma unroll
@@ -484,24 +492,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int nk = (int)(ga.kb / kKS);
 
-    // Each wave copies 8 of the 32 fragment blocks of a stage. Past the last
-    // stage the copy is still issued (from the last stage, into the ring slot
-    // that is never read again) so that the main loop has no branch and the
-    // counter waits stay constant.
+    // DMA copy q of a stage (q = 0..7): waves 0-1 copy A fragment blocks, waves
+    // 2-3 B blocks. Source = wave-uniform block address + stage * 2 KiB + lane
+    // * 16; destination = uniform LDS address (M0). Past the last stage the
+    // copy is still issued (from the last stage, into the ring slot that is
+    // never read again) so the main loop has no branch and the counter waits
+    // stay constant.
+    const bool copies_a = wave < (kFA / kLoadsPerWave);
+    const int8_t *dma_base = copies_a
+        ? ga.RA + (int64_t)l * ga.planeA + (int64_t)tm * (kTileM / 32) * ga.kb * 1024
+        : ga.RB + (int64_t)l * ga.planeB + (int64_t)tn * (kTileN / 32) * ga.kb * 1024;
+    const int fb0 = wave * kLoadsPerWave - (copies_a ? 0 : kFA);  // first fragment block of this wave
+    __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     auto dma = [&](int ks_slot, int q) {
         const int ks = ks_slot < nk ? ks_slot : nk - 1;
-        int8_t *dst = lds + (ks_slot % kNST) * kStageBytes;
-        const int fbi = wave * kLoadsPerWave + q;
-        const int8_t *src;
-        if (fbi < kFA) {
-            const int rb = fbi / kKS, kk = fbi % kKS;
-            src = gA + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
-        } else {
-            const int f2 = fbi - kFA;
-            const int rb = f2 / kKS, kk = f2 % kKS;
-            src = gB + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
-        }
-        __builtin_amdgcn_global_load_lds(src, LDS_PTR(dst + fbi * 1024), 16, 0, 0);
+        const int fb = fb0 + q;  // within A or B
+        const int rb = fb / kKS, kk = fb % kKS;
+        const int8_t *src = dma_base + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
+        __builtin_amdgcn_global_load_lds(src + lane * 16,
+                                         lds3 + (ks_slot % kNST) * kStageBytes + (wave * kLoadsPerWave + q) * 1024,
+                                         16, 0, 0);
     };
     // fragment q of a substep: q < 4 -> A tile q, else B tile q - 4
     auto frag_ptr = [&](const int8_t *stage, int s, int q) {
@@ -829,9 +839,9 @@ static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count +
 static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
 
 hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L, char *ws,
-                            hipStream_t s) {
+                            hipStream_t s, Ev ev) {
     dim3 grid(nblk(m, 64), (unsigned)L.nchunks);
-    hipLaunchKernelGGL(k_row_norms, grid, dim3(256), 0, s, A, m, k, lda, L.kchunk, (double *)(ws + L.part_s),
+    OZ2_LAUNCH(ev, k_row_norms, grid, dim3(256), 0, s, A, m, k, lda, L.kchunk, (double *)(ws + L.part_s),
                        (int *)(ws + L.part_g), (int *)(ws + L.part_bad));
     return hipGetLastError();
 }
@@ -844,21 +854,21 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
 }
 
 hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp, const Layout &L,
-                                char *ws, hipStream_t s) {
-    hipLaunchKernelGGL(k_col_exponents, dim3(nblk(L.n_pad, 4)), dim3(256), 0, s, B, k, n, L.n_pad, ldb, Pp,
+                                char *ws, hipStream_t s, Ev ev) {
+    OZ2_LAUNCH(ev, k_col_exponents, dim3(nblk(L.n_pad, 4)), dim3(256), 0, s, B, k, n, L.n_pad, ldb, Pp,
                        (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
     return hipGetLastError();
 }
 
 hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                         const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad, const Layout &L,
-                        hipStream_t s) {
+                        hipStream_t s, Ev ev) {
     dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
     const int64_t plane = rows_pad * L.k_pad;
     if (k_contiguous)
-        hipLaunchKernelGGL(k_split<true>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
+        OZ2_LAUNCH(ev, k_split<true>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
     else
-        hipLaunchKernelGGL(k_split<false>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
+        OZ2_LAUNCH(ev, k_split<false>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
     return hipGetLastError();
 }
 
@@ -894,11 +904,11 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, const La
 }
 
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc, int8_t *planes,
-                           const Layout &L, hipStream_t s) {
+                           const Layout &L, hipStream_t s, Ev ev) {
     GemmArgs g = gemm_args(RA, RB, nmod, L);
     g.planes = planes;
     const int blocks = g.tiles_m * g.tiles_n * nmod;
-    hipLaunchKernelGGL(k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
+    OZ2_LAUNCH(ev, k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
@@ -923,8 +933,9 @@ hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *ro
     return hipGetLastError();
 }
 
-hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws, hipStream_t s) {
-    hipLaunchKernelGGL(k_accurate_exponents, dim3(nblk(L.m_pad + L.n_pad, 256)), dim3(256), 0, s,
+hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws, hipStream_t s,
+                                     Ev ev) {
+    OZ2_LAUNCH(ev, k_accurate_exponents, dim3(nblk(L.m_pad + L.n_pad, 256)), dim3(256), 0, s,
                        (const int32_t *)(ws + L.rowmax), (const int32_t *)(ws + L.colmax),
                        (const int32_t *)(ws + L.ga), (const int32_t *)(ws + L.gb), m, L.m_pad, n, L.n_pad, Pp,
                        (int32_t *)(ws + L.e), (int32_t *)(ws + L.f));
@@ -932,9 +943,9 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
 }
 
 hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
-                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s) {
+                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
     dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
-    hipLaunchKernelGGL(k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    OZ2_LAUNCH(ev, k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     return hipGetLastError();
 }
 
