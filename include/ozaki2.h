@@ -71,12 +71,19 @@ enum ozaki2_status {
     OZAKI2_SUCCESS = 0,
     OZAKI2_ERR_HIP = 1,         /* a HIP runtime call or kernel launch failed */
     OZAKI2_ERR_WORKSPACE = 2,   /* workspace too small, or its allocation failed */
-    OZAKI2_ERR_UNSUPPORTED = 3  /* k >= 2^17: int32 sums would no longer be exact
-                                   ([Q] section 誤差のないINT8行列積(手順3)) */
+    OZAKI2_ERR_UNSUPPORTED = 3  /* size outside the supported range: k > OZAKI2_MAX_K,
+                                   accurate mode with k > OZAKI2_MAX_K_ACCURATE, m or
+                                   n >= 2^31, or prod_out requested with k >= 2^17 */
 };
 
 #define OZAKI2_MAX_MODULI 20
-#define OZAKI2_MAX_K 131071 /* 2^17 - 1 */
+/* Inner dimension limits. int32 sums of int8 x int8 products are exact only
+ * below 2^17 terms ([Q] section 誤差のないINT8行列積(手順3)); longer inner
+ * dimensions are handled in blocks (the GEMM reduces its accumulators mod p
+ * every 2047 * 64 terms). The accurate-mode bound product (entries <= 64 * 64
+ * per term) stays exact below 2^19 terms. */
+#define OZAKI2_MAX_K ((1 << 22) - 1)
+#define OZAKI2_MAX_K_ACCURATE ((1 << 19) - 1)
 
 /*
  * C := A * B emulated by Ozaki Scheme II ([Q] steps 1-5). Uses a workspace
@@ -122,7 +129,8 @@ int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k,
  *   resB_out int8 [N][n][k]: residues of trunc(2^f_j b_hj), element
  *            (l, j, h) at resB_out[(l*n + j)*k + h];
  *   prod_out int32 [N][n][m]: exact residue products
- *            Q_l(i, j) = sum_h resA(l,i,h) resB(l,j,h) at prod_out[(l*n + j)*m + i], step 3;
+ *            Q_l(i, j) = sum_h resA(l,i,h) resB(l,j,h) at prod_out[(l*n + j)*m + i], step 3
+ *            (only for k < 2^17, where they fit int32);
  *   red_out  uint8 [N][n][m]: Q_l mod p_l in [0, p_l), same indexing.
  * Argument errors as ozaki2_dgemm_ws (workspace_bytes must also cover
  * ozaki2_debug_workspace_size); -13..-18 for a NULL-but-needed debug buffer

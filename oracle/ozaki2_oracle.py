@@ -347,23 +347,28 @@ def scaled_integers(X: np.ndarray, e) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Step 3: one exact integer product per modulus
 # --------------------------------------------------------------------------
+INT32_BLOCK = (1 << 17) - 1  # inner-dimension block for which int8 x int8 sums fit int32
+
+
 def residue_products(RA: np.ndarray, RB: np.ndarray) -> np.ndarray:
-    """Q^(l) = RA^(l) RB^(l)^T for each modulus, int64 [N][m][n].
+    """Q^(l) = RA^(l) RB^(l)^T for each modulus, exact, int64 [N][m][n].
 
     [Q] section 誤差のないINT8行列積(手順3): int8 x int8 products are at most
     128*128 = 16384 in magnitude, so the sums fit int32 while the inner
-    dimension is below 2^17. The product is formed by an FP64 matrix product,
-    which is exact here because every partial sum is an integer below 2^53.
-    RA is [N][m][k], RB is [N][n][k] (B's columns as rows).
+    dimension is below 2^17; larger inner dimensions are split into blocks.
+    Each block product is formed by an FP64 matrix product, which is exact
+    because every partial sum is an integer below 2^31 < 2^53, and the blocks
+    are added in int64. RA is [N][m][k], RB is [N][n][k] (B's columns as rows).
     """
     k = RA.shape[2]
-    if k >= (1 << 17):
-        raise ValueError("inner dimension must be below 2^17")
-    Q = np.empty((RA.shape[0], RA.shape[1], RB.shape[1]), dtype=np.int64)
+    Q = np.zeros((RA.shape[0], RA.shape[1], RB.shape[1]), dtype=np.int64)
     for l in range(RA.shape[0]):
-        ql = RA[l].astype(np.float64) @ RB[l].astype(np.float64).T
-        Q[l] = ql.astype(np.int64)
-    assert np.all(np.abs(Q) < (1 << 31)), "int32 overflow in a residue product"
+        for h0 in range(0, k, INT32_BLOCK):
+            a = RA[l][:, h0:h0 + INT32_BLOCK].astype(np.float64)
+            b = RB[l][:, h0:h0 + INT32_BLOCK].astype(np.float64)
+            qb = (a @ b.T).astype(np.int64)
+            assert np.all(np.abs(qb) < (1 << 31)), "int32 overflow in a block product"
+            Q[l] += qb
     return Q
 
 

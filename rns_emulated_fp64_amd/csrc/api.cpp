@@ -41,10 +41,11 @@ int validate(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, cons
     return 0;
 }
 
-// Sizes are limited so that every offset below fits comfortably in 63 bits.
-bool layout_fits(int64_t m, int64_t n, int64_t k) {
+// Supported sizes: every offset below fits comfortably in 63 bits, the grids
+// fit their dimensions, and the integer products stay exact.
+bool layout_fits(int64_t m, int64_t n, int64_t k, int mode) {
     const int64_t lim = (int64_t)1 << 31;
-    return m < lim && n < lim && k <= OZAKI2_MAX_K;
+    return m < lim && n < lim && k <= (mode == OZAKI2_ACCURATE ? OZAKI2_MAX_K_ACCURATE : OZAKI2_MAX_K);
 }
 
 Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool debug) {
@@ -211,7 +212,8 @@ int front(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const d
           void *stream) {
     int st = validate(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode);
     if (st) return st;
-    if (!layout_fits(m, n, k)) return OZAKI2_ERR_UNSUPPORTED;
+    if (!layout_fits(m, n, k, mode)) return OZAKI2_ERR_UNSUPPORTED;
+    if (dbg && dbg->prod && k >= (1 << 17)) return OZAKI2_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     if (m == 0 || n == 0) return OZAKI2_SUCCESS;
     if (k == 0) {
@@ -262,7 +264,7 @@ size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, in
     if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
                  m > 1 ? m : 1, num_moduli, mode))
         return 0;
-    if (!layout_fits(m, n, k) || m == 0 || n == 0 || k == 0) return 0;
+    if (!layout_fits(m, n, k, mode) || m == 0 || n == 0 || k == 0) return 0;
     return make_layout(m, n, k, num_moduli, mode, false).total;
 }
 
@@ -270,7 +272,7 @@ size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_modu
     if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
                  m > 1 ? m : 1, num_moduli, mode))
         return 0;
-    if (!layout_fits(m, n, k) || m == 0 || n == 0 || k == 0) return 0;
+    if (!layout_fits(m, n, k, mode) || m == 0 || n == 0 || k == 0) return 0;
     return make_layout(m, n, k, num_moduli, mode, true).total;
 }
 
@@ -320,7 +322,8 @@ const char *ozaki2_status_string(int status) {
     case OZAKI2_SUCCESS: return "success";
     case OZAKI2_ERR_HIP: return "HIP runtime or kernel launch error";
     case OZAKI2_ERR_WORKSPACE: return "workspace too small or allocation failed";
-    case OZAKI2_ERR_UNSUPPORTED: return "unsupported size (k must be below 2^17, m and n below 2^31)";
+    case OZAKI2_ERR_UNSUPPORTED:
+        return "unsupported size (k <= 2^22 - 1, or 2^19 - 1 in accurate mode; m, n < 2^31; raw products need k < 2^17)";
     default: break;
     }
     if (status < 0) return "invalid argument (status is minus its 1-based position)";

@@ -308,9 +308,13 @@ __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const 
     }
 }
 
+// Low bytes of a, b, c, d packed little-endian into one word (v_perm_b32:
+// selector bytes 0-3 pick from the second source, 4-7 from the first, 0x0c
+// gives zero).
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-           ((uint32_t)(d & 0xff) << 24);
+    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);  // a0 b0 0 0
+    const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x04000c0cu);  // 0 0 c0 d0
+    return lo | hi;
 }
 
 template <bool KCONTIG>
@@ -424,6 +428,7 @@ constexpr int kFB = (kTileN / 32) * kKS;   // B fragment blocks per stage (16)
 constexpr int kStageBytes = (kFA + kFB) * 1024;
 constexpr int kLoadsPerWave = (kFA + kFB) / 4;
 constexpr int kGroupM = 4;                 // tile rows per raster group
+constexpr int kReduceStages = 2047;        // 2047 * 64 * 2^14 + 128 < 2^31
 static_assert(kKS == 2, "the main loop is written for two substeps per stage");
 static_assert(kLoadsPerWave == 8, "vmcnt immediates below assume 8 DMA loads per wave per stage");
 
@@ -534,7 +539,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // One substep: 16 MFMA slots; slot q also issues fragment read q (q < 8)
     // of the next substep and, in the first substep of a stage, DMA copy q.
     // sched_barrier keeps this exact order.
-    for (int ks = 0; ks < nk; ++ks) {
+    for (int ks_blk = 0; ks_blk < nk; ks_blk += kReduceStages) {
+        const int ks_end = ks_blk + kReduceStages < nk ? ks_blk + kReduceStages : nk;
+        for (int ks = ks_blk; ks < ks_end; ++ks) {
         const int8_t *cur = lds + (ks % kNST) * kStageBytes;
         const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
 #pragma unroll
@@ -558,6 +565,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             __builtin_amdgcn_sched_barrier(0);
             if (q < 8) f0[q] = *(const v4i *)frag_ptr(nxt, 0, q);
             __builtin_amdgcn_sched_barrier(0);
+        }
+        }
+        if (EPI == EPI_MOD && ks_end < nk) {
+            // Inner dimension in blocks ([Q] step 3): after 2047 stages
+            // (131008 terms of at most 2^14) fold the sums back to their
+            // symmetric residues, so they never leave int32.
+            const double p = mc.p[l], pinv = mc.pinv[l];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = smod(acc[i][j][v], p, pinv);
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends

@@ -76,7 +76,8 @@ P = 1 << 20  # a fake non-null pointer: validation fails before it is ever used
         ((4, 4, 4, P, 4, P, 4, P, 4, 21, 0), -10),
         ((4, 4, 4, P, 4, P, 4, P, 4, 8, 2), -11),
         ((4, 4, 4, P, 4, P, 4, P, 4, 8, -1), -11),
-        ((4, 4, 1 << 17, P, 4, P, 1 << 17, P, 4, 8, 0), 3),
+        ((4, 4, 1 << 22, P, 4, P, 1 << 22, P, 4, 8, 0), 3),
+        ((4, 4, 1 << 19, P, 4, P, 1 << 19, P, 4, 8, 1), 3),
         # quick returns: nothing is launched for an empty C
         ((0, 4, 4, 0, 1, P, 4, 0, 1, 8, 0), 0),
         ((4, 0, 4, P, 4, 0, 4, 0, 4, 8, 0), 0),

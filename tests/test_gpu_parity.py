@@ -73,6 +73,16 @@ def test_max_inner_dimension():
     full_parity(A, B, 16, want_prod=True)
 
 
+@pytest.mark.parametrize("k,mode", [((1 << 17) + 4321, "fast"), (400000, "fast"), ((1 << 17) + 4321, "accurate")])
+def test_long_inner_dimension_in_blocks(k, mode):
+    # Beyond 2^17 terms the int32 sums are folded back mod p every 2047 stages
+    # ([Q] step 3: larger inner dimensions are computed in blocks).
+    A, B = W.uniform_case(40, 24, k, seed=k % 97)
+    A[0] = 1.0
+    B[:, 0] = 1.0  # an all-ones row times an all-ones column: |Q| hits its bound
+    full_parity(A, B, 16, mode, want_prod=False)
+
+
 def test_special_values_and_zero_lines():
     A, B = W.spread_case(70, 66, 90, 1.0, seed=5)
     A[3] = 0.0
