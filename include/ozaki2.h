@@ -143,6 +143,27 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
                        int32_t *prod_out, uint8_t *red_out, void *stream);
 
+/*
+ * Test entry point for steps 4 + 5 alone ([Q] sections 秦九韶の大衍求一術 and
+ * 2の累乗による整数化(手順1と5)): C = RN(X) * 2^-(e_i + f_j), X the integer in
+ * (-P/2, P/2] with X = c_l (mod p_l) for every modulus, reconstructed by the
+ * same kernels ozaki2_dgemm uses.
+ *   residues DEVICE uint8 [N][n][m]: c_l of entry (i, j) at
+ *            residues[(l*n + j)*m + i], each in [0, p_l) (not checked);
+ *   e, f     DEVICE int32 [m], [n]: exponents; INT32_MIN makes the row
+ *            (column) NaN;
+ *   C, ldc   DEVICE output, column-major;
+ *   workspace DEVICE, at least ozaki2_workspace_size(m, n, 1, N, OZAKI2_FAST)
+ *            bytes.
+ * Returns 0; -1 m < 0, -2 n < 0, -3 num_moduli outside [2, 20], -4 residues,
+ * -5 e, -6 f or -7 C NULL while needed, -8 ldc < max(1, m), -9 workspace
+ * NULL; OZAKI2_ERR_WORKSPACE if workspace_bytes is too small,
+ * OZAKI2_ERR_UNSUPPORTED for m or n >= 2^31, OZAKI2_ERR_HIP.
+ */
+int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                     const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Workspace bytes for ozaki2_dgemm_debug (larger: raw int32 products). */
 size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
 

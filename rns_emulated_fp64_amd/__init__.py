@@ -27,7 +27,7 @@ EXPORTS = (
     "ozaki2_dgemm", "ozaki2_workspace_size", "ozaki2_dgemm_ws", "ozaki2_dgemm_debug",
     "ozaki2_debug_workspace_size", "ozaki2_max_moduli", "ozaki2_moduli", "ozaki2_scaling_constant",
     "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
-    "ozaki2_finalize",
+    "ozaki2_finalize", "ozaki2_crt_debug",
 )
 
 _lib = None
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_dgemm_ws.restype = i32
     L.ozaki2_dgemm_debug.argtypes = prod + [p, sz, p, p, p, p, p, p, p]
     L.ozaki2_dgemm_debug.restype = i32
+    L.ozaki2_crt_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, sz, p]
+    L.ozaki2_crt_debug.restype = i32
     L.ozaki2_max_moduli.argtypes = []
     L.ozaki2_max_moduli.restype = i32
     L.ozaki2_moduli.argtypes = [i32, p]
@@ -101,6 +103,10 @@ def ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, worksp
                        e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
     return lib().ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace,
                                     workspace_bytes, e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream)
 
 
 def ozaki2_max_moduli() -> int:

@@ -291,6 +291,31 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t
     return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d, stream);
 }
 
+int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                     const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (m < 0) return -1;
+    if (n < 0) return -2;
+    if (num_moduli < 2 || num_moduli > kMaxModuli) return -3;
+    const bool any = m > 0 && n > 0;
+    if (residues == nullptr && any) return -4;
+    if (e == nullptr && any) return -5;
+    if (f == nullptr && any) return -6;
+    if (C == nullptr && any) return -7;
+    if (ldc < (m > 1 ? m : 1)) return -8;
+    if (!any) return OZAKI2_SUCCESS;
+    if (workspace == nullptr) return -9;
+    if (!layout_fits(m, n, 1, OZAKI2_FAST)) return OZAKI2_ERR_UNSUPPORTED;
+    const Layout L = make_layout(m, n, 1, num_moduli, OZAKI2_FAST, false);
+    if (workspace_bytes < L.total) return OZAKI2_ERR_WORKSPACE;
+    const Tables *T = get_tables(num_moduli);
+    hipStream_t s = (hipStream_t)stream;
+    int8_t *planes = (int8_t *)((char *)workspace + L.planes);
+    HIP_TRY(launch_pack_planes(residues, num_moduli, T->mod, m, n, L, planes, s));
+    HIP_TRY(launch_crt(planes, m, n, e, f, T->crt, C, ldc, L, s));
+    return OZAKI2_SUCCESS;
+}
+
 int ozaki2_max_moduli(void) { return kMaxModuli; }
 
 int ozaki2_moduli(int num_moduli, int32_t *out) {

@@ -15,6 +15,7 @@ namespace oz2 {
 constexpr int kMaxModuli = 20;
 constexpr int kChunks = 4;          // CRT weights and P in 40-bit pieces (4 x 40 >= 156 bits)
 constexpr int kChunkBits = 40;
+constexpr int kMaxDigits = 20;      // W_l < P < 2^156 has at most 20 signed base-256 digits
 constexpr int kExpNonfinite = INT32_MIN;  // exponent marker: row/column holds Inf or NaN
 constexpr int kExpEmpty = -4000;          // max-exponent marker of an all-zero row/column
 
@@ -43,6 +44,11 @@ struct CrtConsts {
     double P[kChunks];              // P, 40-bit pieces
     double H[kChunks];              // P / 2, 40-bit pieces
     double pinv120;                 // RN(2^120 / P)
+    double P32[kChunks];            // P in 32-bit pieces (used for P < 2^128)
+    double H32[kChunks];            // P / 2 in 32-bit pieces
+    double pinv96;                  // RN(2^96 / P)
+    int nd;                         // signed base-256 digits of the weights (<= kMaxDigits)
+    int8_t digit[kMaxDigits][32];   // digit[v][l] = v-th digit of W_l, |digit| <= 128; 0 for l >= n
 };
 
 // Constants for the GEMM epilogue (reduction mod p_l).
@@ -103,6 +109,8 @@ hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, 
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
 hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,
                                  const Layout &L, uint8_t *out, hipStream_t s);
+hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
+                              const Layout &L, int8_t *planes, hipStream_t s);
 hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
                                   int32_t *out, hipStream_t s);
 

@@ -476,7 +476,10 @@ __device__ __forceinline__ int smod(int q, double p, double pinv) {
     return (int)fma(-p, rint(y * pinv), y);
 }
 
-template <int EPI>
+// KBLK: the inner dimension spans more than kReduceStages stages and the
+// accumulators are folded between blocks (a separate instance, so that the
+// common case carries no fold code and no register spills).
+template <int EPI, bool KBLK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(GemmArgs ga,
                                                                                          ModConsts mc) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * kStageBytes];
@@ -539,8 +542,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // One substep: 16 MFMA slots; slot q also issues fragment read q (q < 8)
     // of the next substep and, in the first substep of a stage, DMA copy q.
     // sched_barrier keeps this exact order.
-    for (int ks_blk = 0; ks_blk < nk; ks_blk += kReduceStages) {
-        const int ks_end = ks_blk + kReduceStages < nk ? ks_blk + kReduceStages : nk;
+    const int blk_stages = KBLK ? kReduceStages : nk;
+    for (int ks_blk = 0; ks_blk < nk; ks_blk += blk_stages) {
+        const int ks_end = ks_blk + blk_stages < nk ? ks_blk + blk_stages : nk;
         for (int ks = ks_blk; ks < ks_end; ++ks) {
         const int8_t *cur = lds + (ks % kNST) * kStageBytes;
         const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
@@ -567,7 +571,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             __builtin_amdgcn_sched_barrier(0);
         }
         }
-        if (EPI == EPI_MOD && ks_end < nk) {
+        if (KBLK && EPI == EPI_MOD && ks_end < nk) {
             // Inner dimension in blocks ([Q] step 3): after 2047 stages
             // (131008 terms of at most 2^14) fold the sums back to their
             // symmetric residues, so they never leave int32.
@@ -575,9 +579,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[i][j][v] = smod(acc[i][j][v], p, pinv);
+                }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
@@ -657,13 +662,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // hair outside (-P/2, P/2] is corrected on the exact pieces. The integer X is
 // finally rounded to nearest-even from its 160-bit image, so C equals
 // RN(X) * 2^-(e_i + f_j) exactly.
-constexpr double kTwo40 = 0x1p40, kTwoM40 = 0x1p-40;
-
+// Pieces of BITS bits: x = sum_t x[t] 2^(BITS t), each x[t] an integer held
+// exactly in a double. normalize brings x[0..2] into [0, 2^BITS) and leaves the
+// signed remainder in x[3].
+template <int BITS>
 __device__ __forceinline__ void normalize4(double x[4]) {
+    constexpr double base = (double)(1ull << BITS), inv = 1.0 / base;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-        double c = floor(x[t] * kTwoM40);
-        x[t] = fma(-c, kTwo40, x[t]);
+        double c = floor(x[t] * inv);
+        x[t] = fma(-c, base, x[t]);
         x[t + 1] += c;
     }
 }
@@ -674,13 +682,69 @@ __device__ __forceinline__ int sign4(const double x[4]) {
     return (x[2] != 0.0 || x[1] != 0.0 || x[0] != 0.0) ? 1 : 0;
 }
 
+// Exact repair of an estimated quotient: bring X into (-P/2, P/2], with P and
+// H = P/2 in the same pieces as x.
+template <int BITS>
+__device__ __forceinline__ void crt_range_fix(double x[4], const double P[4], const double H[4]) {
+    double z[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[t] = x[t] - H[t];
+    normalize4<BITS>(z);
+    if (sign4(z) > 0) {  // X > P/2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] -= P[t];
+        normalize4<BITS>(x);
+        return;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) z[t] = x[t] + H[t];
+    normalize4<BITS>(z);
+    if (sign4(z) <= 0) {  // X <= -P/2
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] += P[t];
+        normalize4<BITS>(x);
+    }
+}
+
+// X = S - q P with q = round(S / P) from a double estimate; X keeps the sign
+// the estimate predicts (sg) and its magnitude goes to x. The estimate of S / P
+// is good to ~2^-37 absolute, so only |S/P - q| within 2^-30 of 1/2 needs the
+// exact wrap check, which valid scalings never reach; the second check catches
+// |X| below ~2^-37 P, where the predicted sign can be wrong.
+template <int BITS>
+__device__ __forceinline__ void crt_lift(const double S[4], double x[4], double &sg, double s_over_base3,
+                                         const double P[4], const double H[4], double pinv_base3) {
+    const double quo = s_over_base3 * pinv_base3;
+    const double q = rint(quo);
+    const double d = quo - q;  // ~ X / P
+    sg = d < 0.0 ? -1.0 : 1.0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) x[t] = sg * fma(-q, P[t], S[t]);
+    normalize4<BITS>(x);
+    if (fabs(d) > 0.5 - 0x1p-30) {  // near +-P/2: settle the wrap exactly
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] *= sg;
+        crt_range_fix<BITS>(x, P, H);
+        sg = sign4(x) < 0 ? -1.0 : 1.0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] *= sg;
+        normalize4<BITS>(x);
+    }
+    if (x[3] < 0.0) {  // sign predicted wrongly (|X| tiny)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[t] = -x[t];
+        normalize4<BITS>(x);
+        sg = -sg;
+    }
+}
+
 // Integer value of a double holding an integer in [0, 2^52): adding 2^52
 // puts it in the significand field.
 __device__ __forceinline__ uint64_t small_int_bits(double x) {
     return (uint64_t)__double_as_longlong(x + 0x1p52) & ((1ull << 52) - 1);
 }
 
-// RN(x) * 2^-scale_down for a normalized non-negative piece vector
+// RN(x) * 2^-scale_down for a normalized non-negative 40-bit piece vector
 // (x[0..2] in [0, 2^40), x[3] in [0, 2^36)), rounded to nearest-even from the
 // exact 160-bit integer.
 __device__ __forceinline__ double limbs_to_double_rn(const double x[4], int scale_down) {
@@ -709,57 +773,36 @@ __device__ __forceinline__ double limbs_to_double_rn(const double x[4], int scal
     return ldexp((double)mant, scale - lz + 11 - scale_down);
 }
 
-// Exact repair of an estimated quotient: bring X into (-P/2, P/2].
-__device__ __forceinline__ void crt_range_fix(double x[4], const CrtConsts &cc) {
-    double z[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) z[t] = x[t] - cc.H[t];
-    normalize4(z);
-    if (sign4(z) > 0) {  // X > P/2
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] -= cc.P[t];
-        normalize4(x);
-        return;
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) z[t] = x[t] + cc.H[t];
-    normalize4(z);
-    if (sign4(z) <= 0) {  // X <= -P/2
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] += cc.P[t];
-        normalize4(x);
-    }
+// RN(x) * 2^-scale_down for a normalized non-negative 32-bit piece vector
+// (x[t] in [0, 2^32)): the top 64 bits of the 128-bit integer, with the bits
+// below OR-ed into the last place (round to odd), convert to double with a
+// single rounding, which then equals the rounding of the whole integer
+// (64 >= 53 + 2 bits).
+__device__ __forceinline__ double limbs32_to_double_rn(const double x[4], int scale_down) {
+    const uint64_t w0 = ((uint64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
+    const uint64_t w1 = ((uint64_t)(uint32_t)x[3] << 32) | (uint32_t)x[2];
+    if (w1 == 0) return ldexp((double)w0, -scale_down);
+    const int lz = __clzll(w1);
+    const uint64_t top = (w1 << lz) | ((w0 >> 1) >> (63 - lz));
+    const uint64_t odd = (w0 << lz) != 0 ? 1 : 0;
+    return ldexp((double)(top | odd), 64 - lz - scale_down);
 }
 
 __device__ __forceinline__ double crt_finish(const double S[4], int ei, int fj, const CrtConsts &cc) {
-    // S / P estimate (relative error ~2^-51; |S/P| < 2^12)
-    const double s120 = fma(S[0], 0x1p-120, fma(S[1], 0x1p-80, fma(S[2], kTwoM40, S[3])));
-    const double quo = s120 * cc.pinv120;
-    const double q = rint(quo);
-    const double d = quo - q;  // ~ X / P
-    // Work on |X| directly: the sign of X is that of d unless |X| is below
-    // 2^-30 P, which the exact check after normalizing catches.
-    double sg = d < 0.0 ? -1.0 : 1.0;
-    double x[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) x[t] = sg * fma(-q, cc.P[t], S[t]);
-    normalize4(x);
-    if (fabs(d) > 0.5 - 0x1p-30) {  // near +-P/2: settle the wrap exactly (never on valid scalings)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] *= sg;
-        crt_range_fix(x, cc);
-        sg = sign4(x) < 0 ? -1.0 : 1.0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] *= sg;
-        normalize4(x);
-    }
-    if (x[3] < 0.0) {  // sign predicted wrongly (|X| tiny)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = -x[t];
-        normalize4(x);
-        sg = -sg;
-    }
+    // S / 2^120 (|S/P| < 2^12)
+    const double s120 = fma(S[0], 0x1p-120, fma(S[1], 0x1p-80, fma(S[2], 0x1p-40, S[3])));
+    double x[4], sg;
+    crt_lift<40>(S, x, sg, s120, cc.P, cc.H, cc.pinv120);
     const double mag = limbs_to_double_rn(x, ei + fj);
+    return (ei == kExpNonfinite || fj == kExpNonfinite) ? __builtin_nan("") : sg * mag;
+}
+
+// As crt_finish for S in 32-bit pieces (P < 2^128, at most 16 moduli).
+__device__ __forceinline__ double crt_finish32(const double S[4], int ei, int fj, const CrtConsts &cc) {
+    const double s96 = fma(S[0], 0x1p-96, fma(S[1], 0x1p-64, fma(S[2], 0x1p-32, S[3])));
+    double x[4], sg;
+    crt_lift<32>(S, x, sg, s96, cc.P32, cc.H32, cc.pinv96);
+    const double mag = limbs32_to_double_rn(x, ei + fj);
     return (ei == kExpNonfinite || fj == kExpNonfinite) ? __builtin_nan("") : sg * mag;
 }
 
@@ -798,6 +841,73 @@ __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, 
         for (int u = 0; u < kCrtRows; ++u) {
             const int64_t i = i0 + u;
             if (i < m) C[i + j * ldc] = crt_finish(S[u], e[i], fj, cc);
+        }
+    }
+}
+
+// The weighted sum S = sum_l c_l W_l on the matrix cores (up to 16 moduli).
+// Each weight is written in signed base-256 digits, W_l = sum_v d_lv 256^v
+// with |d_lv| <= 128 (16 digits suffice below 2^127), so the digit sums
+// D_v = sum_l c_l d_lv are products of int8 matrices, exact in int32
+// (|D_v| <= 16 * 128 * 128 = 2^18). One v_mfma_i32_32x32x32_i8 forms them for
+// 64 entries at once: lane L supplies the 16 residues of its own entry as the
+// B operand (column L % 32, k-half L / 32), and the A operand holds the digits
+// only in the rows whose half of the accumulator layout ((row / 4) odd or
+// even) matches that k-half, so lane L gets back exactly the 16 digit sums of
+// its own entry, digit v in register v. S is then assembled from the D_v into
+// four exact 32-bit pieces (|piece| < 2^42.1) for crt_finish32.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_crt_mma(const int8_t *__restrict__ planes, int64_t plane_elems,
+                                                 int64_t m_pad, int64_t m, int64_t n,
+                                                 const int32_t *__restrict__ e, const int32_t *__restrict__ f,
+                                                 CrtConsts cc, double *__restrict__ C, int64_t ldc) {
+    __shared__ __attribute__((aligned(16))) int8_t digit[16][16];
+    if (threadIdx.x < 64) {
+        const int v = threadIdx.x >> 2, b4 = (threadIdx.x & 3) * 4;
+        *(uint32_t *)&digit[v][b4] = *(const uint32_t *)&cc.digit[v][b4];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 31;
+    const bool mine = ((r >> 2) & 1) == (lane >> 5);
+    const v4i aop = mine ? *(const v4i *)&digit[4 * (r >> 3) + (r & 3)][0] : (v4i){0, 0, 0, 0};
+
+    // four consecutive rows per lane; a wavefront covers 256 rows, which lie
+    // either all inside or all outside the padded plane (m_pad % 256 == 0), so
+    // the MFMAs always run on full wavefronts
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i0;
+        uint32_t w[16];
+#pragma unroll
+        for (int l = 0; l < 16; ++l) w[l] = l < cc.n ? *(const uint32_t *)(src + (int64_t)l * plane_elems) : 0u;
+        // 4 x 4 byte transposes: R[u] = residues of row i0 + u, moduli 0..15
+        v4i R[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint32_t a0 = w[4 * g], a1 = w[4 * g + 1], a2 = w[4 * g + 2], a3 = w[4 * g + 3];
+            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.0 a1.0 a0.1 a1.1
+            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.2 a1.2 a0.3 a1.3
+            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+            R[0][g] = (int)__builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+            R[1][g] = (int)__builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+            R[2][g] = (int)__builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+            R[3][g] = (int)__builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+        }
+        const int fj = f[j];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, R[u], (v16i){0}, 0, 0, 0);
+            // 32-bit pieces S_t = D_4t + D_4t+1 2^8 + D_4t+2 2^16 + D_4t+3 2^24:
+            // digit pairs in int32 (|.| < 2^26.1), then one exact fma
+            double S[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int lo = D[4 * t] + D[4 * t + 1] * 256, hi = D[4 * t + 2] + D[4 * t + 3] * 256;
+                S[t] = fma((double)hi, 65536.0, (double)lo);
+            }
+            const int64_t i = i0 + u;
+            if (i < m) C[i + j * ldc] = crt_finish32(S, e[i], fj, cc);
         }
     }
 }
@@ -849,6 +959,20 @@ __global__ void k_copy_planes_red(const int8_t *planes, int64_t m, int64_t m_pad
         if (p == 256) v &= 0xff;
         else if (v < 0) v += p;
         out[(l * n + j) * m + i] = (uint8_t)v;
+    }
+}
+
+// [0, p) -> symmetric residues in the padded plane layout (padding zeroed)
+__global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t m_pad, int64_t plane_elems,
+                              ModConsts mc, int8_t *planes) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t l = blockIdx.z;
+    if (i >= m_pad) return;
+    const int p = (int)mc.p[l];
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        int v = i < m ? res[(l * n + j) * m + i] : 0;
+        if (v > (p - 1) / 2) v -= p;
+        planes[l * plane_elems + j * m_pad + i] = (int8_t)v;
     }
 }
 
@@ -928,7 +1052,13 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const M
     GemmArgs g = gemm_args(RA, RB, nmod, L);
     g.planes = planes;
     const int blocks = g.tiles_m * g.tiles_n * nmod;
-    OZ2_LAUNCH(ev, k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
+    if (g.kb / kKS > kReduceStages) {
+        auto kern = k_gemm<EPI_MOD, true>;
+        OZ2_LAUNCH(ev, kern, dim3(blocks), dim3(256), 0, s, g, mc);
+    } else {
+        auto kern = k_gemm<EPI_MOD, false>;
+        OZ2_LAUNCH(ev, kern, dim3(blocks), dim3(256), 0, s, g, mc);
+    }
     return hipGetLastError();
 }
 
@@ -938,7 +1068,7 @@ hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t
     g.raw = raw;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n * nmod;
-    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL((k_gemm<EPI_RAW, false>), dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
@@ -949,7 +1079,7 @@ hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *ro
     g.colmax = colmax;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL((k_gemm<EPI_BOUND, false>), dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
@@ -965,7 +1095,20 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
 hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
     dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
-    OZ2_LAUNCH(ev, k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    if (cc.n <= 16 && cc.nd <= 16) {
+        OZ2_LAUNCH(ev, k_crt_mma, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    } else {
+        // 17..20 moduli: the 2 x 2 MFMA blocks are mostly padding there, and
+        // the FMA form measures slightly faster on MI355X
+        OZ2_LAUNCH(ev, k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
+                              const Layout &L, int8_t *planes, hipStream_t s) {
+    dim3 grid(nblk(L.m_pad, 256), ydim(n), (unsigned)nmod);
+    hipLaunchKernelGGL(k_pack_planes, grid, dim3(256), 0, s, residues, m, n, L.m_pad, L.m_pad * L.n_pad, mc, planes);
     return hipGetLastError();
 }
 

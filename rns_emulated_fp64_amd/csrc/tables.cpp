@@ -9,6 +9,7 @@
 #include "tables.h"
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -55,6 +56,16 @@ struct U256 {
     uint32_t mod_small(uint32_t f) const {
         uint32_t r;
         div_small(f, &r);
+        return r;
+    }
+    U256 add_small(uint32_t a) const {
+        U256 r = *this;
+        uint64_t carry = a;
+        for (int i = 0; i < 8 && carry; ++i) {
+            uint64_t t = (uint64_t)r.d[i] + carry;
+            r.d[i] = (uint32_t)t;
+            carry = t >> 32;
+        }
         return r;
     }
     U256 sub_one() const {  // *this - 1, *this > 0
@@ -164,6 +175,17 @@ void build(Tables &t, int n) {
         U256 W = M.mul_small(K);
         std::memcpy(t.weight[l], W.d, sizeof(W.d));
         chunks40(W, t.crt.w[l]);
+        // signed base-256 digits, least significant first: W = sum_v d_v 256^v
+        U256 rest = W;
+        for (int v = 0; !rest.is_zero(); ++v) {
+            if (v >= kMaxDigits) std::abort();  // cannot happen for P < 2^159
+            uint32_t low = rest.d[0] & 0xffu;
+            int d = low >= 128 ? (int)low - 256 : (int)low;
+            rest = rest.div_small(256, nullptr);
+            if (d < 0) rest = rest.add_small(1);
+            t.crt.digit[v][l] = (int8_t)d;
+            if (v + 1 > t.crt.nd) t.crt.nd = v + 1;
+        }
     }
     chunks40(P, t.crt.P);
     U256 H = P.div_small(2, nullptr);
@@ -172,6 +194,11 @@ void build(Tables &t, int n) {
     long double Pld = 0.0L;
     for (int i = 7; i >= 0; --i) Pld = Pld * 4294967296.0L + (long double)P.d[i];
     t.crt.pinv120 = (double)(ldexpl(1.0L, 120) / Pld);
+    t.crt.pinv96 = (double)(ldexpl(1.0L, 96) / Pld);
+    for (int c = 0; c < kChunks; ++c) {  // 32-bit pieces (the low 128 bits)
+        t.crt.P32[c] = (double)P.d[c];
+        t.crt.H32[c] = (double)H.d[c];
+    }
 }
 
 std::mutex g_mu;

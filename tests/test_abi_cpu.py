@@ -102,6 +102,28 @@ def test_workspace_checks():
     assert oz.ozaki2_debug_workspace_size(300, 200, 500, 8, 0) > oz.ozaki2_workspace_size(300, 200, 500, 8, 0)
 
 
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((-1, 4, 8, P, P, P, P, 4, P, 1 << 40), -1),
+        ((4, -1, 8, P, P, P, P, 4, P, 1 << 40), -2),
+        ((4, 4, 1, P, P, P, P, 4, P, 1 << 40), -3),
+        ((4, 4, 21, P, P, P, P, 4, P, 1 << 40), -3),
+        ((4, 4, 8, 0, P, P, P, 4, P, 1 << 40), -4),
+        ((4, 4, 8, P, 0, P, P, 4, P, 1 << 40), -5),
+        ((4, 4, 8, P, P, 0, P, 4, P, 1 << 40), -6),
+        ((4, 4, 8, P, P, P, 0, 4, P, 1 << 40), -7),
+        ((4, 4, 8, P, P, P, P, 3, P, 1 << 40), -8),
+        ((4, 4, 8, P, P, P, P, 4, 0, 1 << 40), -9),
+        ((4, 4, 8, P, P, P, P, 4, P, 16), 2),
+        ((1 << 31, 4, 8, P, P, P, P, 1 << 31, P, 1 << 60), 3),
+        ((0, 4, 8, 0, 0, 0, 0, 1, 0, 0), 0),
+    ],
+)
+def test_crt_debug_status_codes(args, status):
+    assert oz.ozaki2_crt_debug(*args, 0) == status
+
+
 def test_status_strings():
     for s in (0, 1, 2, 3, -4, 99):
         assert isinstance(oz.status_string(s), str) and oz.status_string(s)
