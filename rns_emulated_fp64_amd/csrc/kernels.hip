@@ -430,7 +430,9 @@ constexpr int kLoadsPerWave = (kFA + kFB) / 4;
 constexpr int kGroupM = 4;                 // tile rows per raster group
 constexpr int kReduceStages = 2047;        // 2047 * 64 * 2^14 + 128 < 2^31
 static_assert(kKS == 2, "the main loop is written for two substeps per stage");
-static_assert(kLoadsPerWave == 8, "vmcnt immediates below assume 8 DMA loads per wave per stage");
+// DMA copies a wave may leave in flight at a stage barrier: kNST-2 stages
+#define OZ2_GEMM_VMCNT "16"
+static_assert((kNST - 2) * kLoadsPerWave == 16, "OZ2_GEMM_VMCNT must equal (kNST - 2) * kLoadsPerWave");
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -510,14 +512,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int8_t *dma_base = copies_a
         ? ga.RA + (int64_t)l * ga.planeA + (int64_t)tm * (kTileM / 32) * ga.kb * 1024
         : ga.RB + (int64_t)l * ga.planeB + (int64_t)tn * (kTileN / 32) * ga.kb * 1024;
-    const int fb0 = wave * kLoadsPerWave - (copies_a ? 0 : kFA);  // first fragment block of this wave
+    // This wave's copies q = 2r, 2r + 1 are the two 32-wide halves (kk = 0, 1)
+    // of fragment row block rb0 + r: a wave-uniform row pointer plus a
+    // per-lane 32-bit offset, so each copy needs one scalar pointer update.
+    const int rb0 = (wave * kLoadsPerWave - (copies_a ? 0 : kFA)) / kKS;
+    const int8_t *dma_row[kLoadsPerWave / kKS];
+#pragma unroll
+    for (int r = 0; r < kLoadsPerWave / kKS; ++r) dma_row[r] = dma_base + (int64_t)(rb0 + r) * ga.kb * 1024;
+    const uint32_t lane_off[kKS] = {(uint32_t)lane * 16, (uint32_t)lane * 16 + 1024};
     __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     auto dma = [&](int ks_slot, int q) {
         const int ks = ks_slot < nk ? ks_slot : nk - 1;
-        const int fb = fb0 + q;  // within A or B
-        const int rb = fb / kKS, kk = fb % kKS;
-        const int8_t *src = dma_base + ((int64_t)rb * ga.kb + (int64_t)ks * kKS + kk) * 1024;
-        __builtin_amdgcn_global_load_lds(src + lane * 16,
+        const int8_t *src = dma_row[q / kKS] + (int64_t)ks * (kKS * 1024);
+        __builtin_amdgcn_global_load_lds(src + lane_off[q % kKS],
                                          lds3 + (ks_slot % kNST) * kStageBytes + (wave * kLoadsPerWave + q) * 1024,
                                          16, 0, 0);
     };
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int st = 0; st < kNST - 1; ++st)
 #pragma unroll
         for (int q = 0; q < kLoadsPerWave; ++q) dma(st, q);
-    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");  // kNST-2 stages stay in flight
+    asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ")\n\ts_barrier" ::: "memory");  // kNST-2 stages stay in flight
 
     v4i f0[8], f1[8];  // fragments of the current / next substep: A tiles 0..3, B tiles 0..3
 #pragma unroll
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         // end of stage: the next stage must have landed and every wave must be
         // done reading this buffer before anyone refills it
-        asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
         // substep 1; reads fetch substep 0 of the next stage (on the last stage
         // a stale but valid buffer whose values are never used)
 #pragma unroll
