@@ -196,8 +196,10 @@ const char *ozaki2_status_string(int status);
 
 /*
  * Per-phase timing with HIP events recorded on the caller's stream right
- * before the first and right after the last kernel of a phase (phases: 0
- * scaling/exponents, 1 residue split, 2 INT8 GEMMs, 3 CRT + unscale).
+ * before and right after each run of consecutive kernels of one phase
+ * (phases: 0 scaling/exponents, 1 residue split, 2 INT8 GEMMs, 3 CRT +
+ * unscale; fast mode scales and splits A before it scales B, so phases 0 and
+ * 1 are each timed as two runs and summed).
  * ozaki2_timing_enable(max_calls, all_phases) creates events for up to
  * max_calls product calls (max_calls <= 0 turns timing off); with
  * all_phases == 0 only phase 2 is timed, which keeps the extra stream time to

@@ -94,9 +94,14 @@ Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool deb
 }
 
 // ---- timing ---------------------------------------------------------------
+// Each call records up to kMaxIntervals intervals (a start and a stop event
+// around one or more consecutive launches of one phase); the phase of each
+// interval is kept in tag (-1 = unused).
+constexpr int kMaxIntervals = 8;
 struct Timing {
     std::mutex mu;
-    std::vector<hipEvent_t> ev;  // 2 * kNumPhases per call: start, stop of each phase
+    std::vector<hipEvent_t> ev;  // 2 * kMaxIntervals per call
+    std::vector<int> tag;        // kMaxIntervals per call
     int max_calls = 0;
     int used = 0;
     bool all_phases = false;  // false: only the GEMM phase is timed
@@ -106,15 +111,20 @@ Timing g_timing;
 void timing_free_locked() {
     for (hipEvent_t e : g_timing.ev) (void)hipEventDestroy(e);
     g_timing.ev.clear();
+    g_timing.tag.clear();
     g_timing.max_calls = 0;
     g_timing.used = 0;
 }
 
-// Event slots for one call, or nullptr when timing is off or full.
-hipEvent_t *timing_slots() {
+// Event and tag slots for one call, or nullptrs when timing is off or full.
+void timing_slots(hipEvent_t **ev, int **tag) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    if (g_timing.used >= g_timing.max_calls) return nullptr;
-    return &g_timing.ev[(size_t)(g_timing.used++) * (2 * kNumPhases)];
+    *ev = nullptr;
+    *tag = nullptr;
+    if (g_timing.used >= g_timing.max_calls) return;
+    const size_t c = (size_t)(g_timing.used++);
+    *ev = &g_timing.ev[c * (2 * kMaxIntervals)];
+    *tag = &g_timing.tag[c * kMaxIntervals];
 }
 
 // ---- cached workspace per device ------------------------------------------
@@ -144,24 +154,34 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
     // after the last kernel of a phase; unless all phases were asked for, only
     // the GEMM phase is timed (each record costs a few microseconds of stream
     // time).
-    hipEvent_t *ev = timing_slots();
+    hipEvent_t *ev = nullptr;
+    int *tag = nullptr;
+    timing_slots(&ev, &tag);
     const bool all_phases = g_timing.all_phases;
+    int nint = 0, open = -1;
     auto ev_of = [&](int phase, bool first, bool last) {
         Ev e;
-        if (ev && (all_phases || phase == kPhaseGemm)) {
-            if (first) e.start = ev[2 * phase];
-            if (last) e.stop = ev[2 * phase + 1];
+        if (!ev || !(all_phases || phase == kPhaseGemm)) return e;
+        if (first && nint < kMaxIntervals) {
+            open = nint++;
+            tag[open] = phase;
+            e.start = ev[2 * open];
+        }
+        if (last && open >= 0) {
+            e.stop = ev[2 * open + 1];
+            open = -1;
         }
         return e;
     };
     const bool accurate = mode == OZAKI2_ACCURATE;
 
-    // Step 1: exponents ([G] Methodik for fast mode; accurate mode bounds the
-    // products with one extra INT8 GEMM first).
-    HIP_TRY(launch_row_norms(A, m, k, lda, L, ws, s, ev_of(kPhaseScale, true, false)));
-    HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
-    HIP_TRY(launch_col_exponents(B, k, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, false, !accurate)));
+    // Step 1: squared norms of the rows of A and exponents of the columns of
+    // B ([G] Methodik), one launch.
+    HIP_TRY(launch_scale(A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
     if (accurate) {
+        // Accurate mode bounds the products with one extra INT8 GEMM first
+        // ([G] Problemstellung).
+        HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
         HIP_TRY(launch_quantize(A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
                                 L.m_pad, L, s));
         HIP_TRY(launch_quantize(B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
@@ -173,12 +193,11 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
         HIP_TRY(launch_accurate_exponents(m, n, T->Pp, L, ws, s, ev_of(kPhaseScale, false, true)));
     }
 
-    // Steps 1 + 2: integerize and split into residues.
+    // Steps 1 + 2: integerize and split both operands into residues, one
+    // launch (in fast mode it also finishes the row exponents of A).
+    HIP_TRY(launch_split(A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
+                         ev_of(kPhaseSplit, true, true)));
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
-    HIP_TRY(launch_split(A, m, k, lda, false, e, T->split, (int8_t *)(ws + L.ra), L.m_pad, L, s,
-                         ev_of(kPhaseSplit, true, false)));
-    HIP_TRY(launch_split(B, n, k, ldb, true, f, T->split, (int8_t *)(ws + L.rb), L.n_pad, L, s,
-                         ev_of(kPhaseSplit, false, true)));
 
     // Step 3: one exact INT8 product per modulus, reduced mod p_l.
     HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, T->mod,
@@ -360,10 +379,12 @@ int ozaki2_timing_enable(int max_calls, int all_phases) {
     timing_free_locked();
     g_timing.all_phases = all_phases != 0;
     if (max_calls <= 0) return OZAKI2_SUCCESS;
-    g_timing.ev.resize((size_t)max_calls * (2 * kNumPhases));
+    g_timing.ev.resize((size_t)max_calls * (2 * kMaxIntervals), nullptr);
+    g_timing.tag.assign((size_t)max_calls * kMaxIntervals, -1);
     for (hipEvent_t &e : g_timing.ev) {
         if (hipEventCreate(&e) != hipSuccess) {
             e = nullptr;
+            timing_free_locked();
             return OZAKI2_ERR_HIP;
         }
     }
@@ -376,14 +397,15 @@ int ozaki2_timing_read(double *ms_out, int *calls) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     double acc[kNumPhases] = {0, 0, 0, 0};
     for (int c = 0; c < g_timing.used; ++c) {
-        hipEvent_t *ev = &g_timing.ev[(size_t)c * (2 * kNumPhases)];
-        if (hipEventSynchronize(ev[2 * kPhaseGemm + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
-        for (int p = 0; p < kNumPhases; ++p) {
-            if (!g_timing.all_phases && p != kPhaseGemm) continue;
-            if (g_timing.all_phases && hipEventSynchronize(ev[2 * p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
+        hipEvent_t *ev = &g_timing.ev[(size_t)c * (2 * kMaxIntervals)];
+        int *tag = &g_timing.tag[(size_t)c * kMaxIntervals];
+        for (int t = 0; t < kMaxIntervals; ++t) {
+            if (tag[t] < 0) continue;
+            if (hipEventSynchronize(ev[2 * t + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
             float ms = 0.f;
-            if (hipEventElapsedTime(&ms, ev[2 * p], ev[2 * p + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
-            acc[p] += ms;
+            if (hipEventElapsedTime(&ms, ev[2 * t], ev[2 * t + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
+            acc[tag[t]] += ms;
+            tag[t] = -1;
         }
     }
     if (ms_out)

@@ -82,14 +82,12 @@ struct Ev {
 };
 
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
-hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L,
-                            char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s);
-hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp,
-                                const Layout &L, char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                        const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad,
-                        const Layout &L, hipStream_t s, Ev ev = {});
+hipError_t launch_scale(const double *A, int64_t m, int64_t k, int64_t lda, const double *B, int64_t n,
+                        int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
+hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
+hipError_t launch_split(const double *A, int64_t m, int64_t lda, const double *B, int64_t n, int64_t ldb,
+                        int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L,
+                        char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                            const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
                            hipStream_t s);

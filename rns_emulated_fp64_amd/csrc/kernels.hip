@@ -84,15 +84,15 @@ __device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
 // each thread accumulates every 4th column of its chunk, and the 4 lanes of a
 // row are merged in a fixed order through LDS. Output: one partial
 // (s, g, nonfinite) per (chunk, row).
-__global__ __launch_bounds__(256) void k_row_norms(const double *__restrict__ A, int64_t m, int64_t k,
-                                                   int64_t lda, int64_t kchunk, double *__restrict__ ps,
-                                                   int *__restrict__ pg, int *__restrict__ pbad) {
+__device__ __forceinline__ void row_norms_block(const double *__restrict__ A, int64_t m, int64_t k, int64_t lda,
+                                                int64_t kchunk, double *__restrict__ ps, int *__restrict__ pg,
+                                                int *__restrict__ pbad, int64_t rowblock, int64_t chunk) {
     __shared__ double sh_s[4][64];
     __shared__ int sh_g[4][64];
     __shared__ int sh_b[4][64];
     const int r = threadIdx.x & 63, kl = threadIdx.x >> 6;
-    const int64_t i = (int64_t)blockIdx.x * 64 + r;
-    const int64_t h0 = (int64_t)blockIdx.y * kchunk;
+    const int64_t i = rowblock * 64 + r;
+    const int64_t h0 = chunk * kchunk;
     const int64_t h1 = h0 + kchunk < k ? h0 + kchunk : k;
     double s = 0.0;
     int g = kExpEmpty;
@@ -127,54 +127,76 @@ __global__ __launch_bounds__(256) void k_row_norms(const double *__restrict__ A,
             ssq_merge(s, g, sh_s[q][r], sh_g[q][r]);
             bad |= sh_b[q][r];
         }
-        const int64_t o = (int64_t)blockIdx.y * m + i;
+        const int64_t o = chunk * m + i;
         ps[o] = s;
         pg[o] = g;
         pbad[o] = bad;
     }
 }
 
-// Combine the chunks of each row in ascending order; e = fast exponent,
-// ga = max exponent (the r_i of accurate mode). Rows in [m, m_pad) get 0.
+// Exponent of row i from its chunk partials, merged in ascending chunk order:
+// e = fast exponent, g = max exponent (the r_i of accurate mode).
+__device__ __forceinline__ void row_exponent_from_partials(const double *__restrict__ ps,
+                                                           const int *__restrict__ pg,
+                                                           const int *__restrict__ pbad, int64_t m, int64_t i,
+                                                           int nchunks, double Pp, int &e, int &g_out) {
+    double s = 0.0;
+    int g = kExpEmpty;
+    int bad = 0;
+    // loads in batches of 8 (all issued before the merges), merges in
+    // ascending chunk order
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+        double vs[8];
+        int vg[8], vb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t o = (int64_t)(c0 + u < nchunks ? c0 + u : c0) * m + i;
+            vs[u] = ps[o];
+            vg[u] = pg[o];
+            vb[u] = pbad[o];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (c0 + u < nchunks) {
+                bad |= vb[u];
+                ssq_merge(s, g, vs[u], vg[u]);
+            }
+        }
+    }
+    if (bad) {
+        e = kExpNonfinite;
+        g_out = kExpNonfinite;
+    } else if (s == 0.0) {
+        e = 0;
+        g_out = 0;
+    } else {
+        e = exponent_from_bound(s, Pp) - g;
+        g_out = g;
+    }
+}
+
+// Row exponents of every row from the chunk partials (accurate mode, which
+// needs them before the bound product). Rows in [m, m_pad) get 0.
 __global__ __launch_bounds__(256) void k_row_exponents(const double *__restrict__ ps, const int *__restrict__ pg,
                                                        const int *__restrict__ pbad, int64_t m, int64_t m_pad,
                                                        int nchunks, double Pp, int32_t *__restrict__ e,
                                                        int32_t *__restrict__ ga) {
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= m_pad) return;
-    if (i >= m) {
-        e[i] = 0;
-        ga[i] = 0;
-        return;
-    }
-    double s = 0.0;
-    int g = kExpEmpty;
-    int bad = 0;
-    for (int c = 0; c < nchunks; ++c) {
-        int64_t o = (int64_t)c * m + i;
-        bad |= pbad[o];
-        ssq_merge(s, g, ps[o], pg[o]);
-    }
-    if (bad) {
-        e[i] = kExpNonfinite;
-        ga[i] = kExpNonfinite;
-    } else if (s == 0.0) {
-        e[i] = 0;
-        ga[i] = 0;
-    } else {
-        e[i] = exponent_from_bound(s, Pp) - g;
-        ga[i] = g;
-    }
+    int ev = 0, gv = 0;
+    if (i < m) row_exponent_from_partials(ps, pg, pbad, m, i, nchunks, Pp, ev, gv);
+    e[i] = ev;
+    ga[i] = gv;
 }
 
 // Columns of column-major B (contiguous): one wavefront per column, lanes
 // stride the column, then a fixed xor-butterfly merge (every lane ends with
 // the same bits).
-__global__ __launch_bounds__(256) void k_col_exponents(const double *__restrict__ B, int64_t k, int64_t n,
-                                                       int64_t n_pad, int64_t ldb, double Pp,
-                                                       int32_t *__restrict__ f, int32_t *__restrict__ gb) {
+__device__ __forceinline__ void col_exponents_block(const double *__restrict__ B, int64_t k, int64_t n,
+                                                    int64_t n_pad, int64_t ldb, double Pp, int32_t *__restrict__ f,
+                                                    int32_t *__restrict__ gb, int64_t blk) {
     const int lane = threadIdx.x & 63;
-    int64_t j = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int64_t j = blk * 4 + (threadIdx.x >> 6);
     if (j >= n_pad) return;
     if (j >= n) {
         if (lane == 0) {
@@ -225,6 +247,21 @@ __global__ __launch_bounds__(256) void k_col_exponents(const double *__restrict_
             gb[j] = g;
         }
     }
+}
+
+// Step 1 for both operands in one launch: blocks [0, nA) are row-norm blocks
+// of A (row block fastest, then k-chunk), the rest column blocks of B.
+__global__ __launch_bounds__(256) void k_scale(const double *__restrict__ A, int64_t m, int64_t k, int64_t lda,
+                                               int64_t kchunk, int64_t rowblocks, int64_t nA,
+                                               double *__restrict__ ps, int *__restrict__ pg,
+                                               int *__restrict__ pbad, const double *__restrict__ B, int64_t n,
+                                               int64_t n_pad, int64_t ldb, double Pp, int32_t *__restrict__ f,
+                                               int32_t *__restrict__ gb) {
+    const int64_t bid = blockIdx.x;
+    if (bid < nA)
+        row_norms_block(A, m, k, lda, kchunk, ps, pg, pbad, bid % rowblocks, bid / rowblocks);
+    else
+        col_exponents_block(B, k, n, n_pad, ldb, Pp, f, gb, bid - nA);
 }
 
 // Accurate mode: e_i = floor(P' + 6 - r_i - 0.5 (log2 R_i + 4 u32)) with R_i
@@ -317,19 +354,21 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
     return lo | hi;
 }
 
-template <bool KCONTIG>
-__global__ __launch_bounds__(256) void k_split(const double *__restrict__ X, int64_t rows, int64_t kdim,
-                                               int64_t ld, const int32_t *__restrict__ ex, SplitConsts sc,
-                                               int8_t *__restrict__ out, int64_t plane_bytes, int64_t kb) {
-    __shared__ double tile[kSplitRows][kSplitLd];
-    const int64_t r0 = (int64_t)blockIdx.x * kSplitRows, h0 = (int64_t)blockIdx.y * kSplitCols;
+// One split block: rows [bx*32, +32) x K [by*128, +128) of X (KCONTIG: K
+// runs along memory). ex_row(rr) gives the exponent of row bx*32 + rr.
+template <bool KCONTIG, class ExpOf>
+__device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const double *__restrict__ X, int64_t rows,
+                                            int64_t kdim, int64_t ld, ExpOf ex_row, const SplitConsts &sc,
+                                            int8_t *__restrict__ out, int64_t plane_bytes, int64_t kb, int64_t bx,
+                                            int64_t by) {
+    const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
     split_load_tile<KCONTIG>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
 
     const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
     const int kk0 = fb * 32 + 16 * (lane >> 5);
     const int64_t r = r0 + rr;
-    int e = r < rows ? ex[r] : 0;
+    int e = r < rows ? ex_row(rr) : 0;
     const bool zero = (e == kExpNonfinite);
     if (zero) e = 0;
 
@@ -347,7 +386,7 @@ __global__ __launch_bounds__(256) void k_split(const double *__restrict__ X, int
         d0[u] = fma(-hi, 0x1p42, x);
     }
 
-    int8_t *dst = out + ((int64_t)blockIdx.x * kb + (int64_t)blockIdx.y * 4 + fb) * 1024 + lane * 16;
+    int8_t *dst = out + (bx * kb + by * 4 + fb) * 1024 + lane * 16;
     // modulus 256: x = d0 (mod 256); residue in [-128, 128], 128 and -128 share the low byte
     {
         int v[16];
@@ -374,6 +413,49 @@ __global__ __launch_bounds__(256) void k_split(const double *__restrict__ X, int
         w.z = pack4(v[8], v[9], v[10], v[11]);
         w.w = pack4(v[12], v[13], v[14], v[15]);
         *(uint4 *)(dst + l * plane_bytes) = w;
+    }
+}
+
+// Steps 1 + 2 for both operands in one launch: blocks [0, nA) split A (row
+// tile fastest, then K tile), the rest split B. FOLD: fast mode, where the
+// exponents of A's rows are merged here from the row-norm partials (the first
+// K tile of each row tile also stores them for the reconstruction); otherwise
+// they are read from e.
+template <bool FOLD>
+__global__ __launch_bounds__(256) void k_split(const double *__restrict__ A, int64_t m, int64_t lda,
+                                               const double *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
+                                               int64_t tilesA, int64_t tilesB, int64_t nA,
+                                               const double *__restrict__ ps,
+                                               const int *__restrict__ pg, const int *__restrict__ pbad,
+                                               int nchunks, double Pp, int32_t *__restrict__ e,
+                                               const int32_t *__restrict__ f, SplitConsts sc,
+                                               int8_t *__restrict__ RA, int64_t planeA, int8_t *__restrict__ RB,
+                                               int64_t planeB, int64_t kb) {
+    __shared__ double tile[kSplitRows][kSplitLd];
+    __shared__ int sh_e[kSplitRows];
+    const int64_t bid = blockIdx.x;
+    if (bid < nA) {
+        const int64_t bx = bid % tilesA, by = bid / tilesA;
+        if (FOLD) {
+            if (threadIdx.x < kSplitRows) {
+                const int64_t i = bx * kSplitRows + threadIdx.x;
+                int ev = 0, gv = 0;
+                if (i < m) row_exponent_from_partials(ps, pg, pbad, m, i, nchunks, Pp, ev, gv);
+                sh_e[threadIdx.x] = ev;
+                if (by == 0) e[i] = ev;  // i < m_pad: the workspace holds m_pad entries
+            }
+            // split_block's barrier after the tile load orders these LDS writes
+            split_block<false>(tile, A, m, kdim, lda, [&](int rr) { return sh_e[rr]; }, sc, RA, planeA, kb, bx, by);
+        } else {
+            const int32_t *er = e + bx * kSplitRows;
+            split_block<false>(tile, A, m, kdim, lda, [&](int rr) { return (int)er[rr]; }, sc, RA, planeA, kb, bx,
+                               by);
+        }
+    } else {
+        const int64_t b = bid - nA;
+        const int64_t bx = b % tilesB, by = b / tilesB;
+        const int32_t *fr = f + bx * kSplitRows;
+        split_block<true>(tile, B, n, kdim, ldb, [&](int rr) { return (int)fr[rr]; }, sc, RB, planeB, kb, bx, by);
     }
 }
 
@@ -989,37 +1071,42 @@ __global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t 
 static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count + per - 1) / per); }
 static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
 
-hipError_t launch_row_norms(const double *A, int64_t m, int64_t k, int64_t lda, const Layout &L, char *ws,
-                            hipStream_t s, Ev ev) {
-    dim3 grid(nblk(m, 64), (unsigned)L.nchunks);
-    OZ2_LAUNCH(ev, k_row_norms, grid, dim3(256), 0, s, A, m, k, lda, L.kchunk, (double *)(ws + L.part_s),
-                       (int *)(ws + L.part_g), (int *)(ws + L.part_bad));
+hipError_t launch_scale(const double *A, int64_t m, int64_t k, int64_t lda, const double *B, int64_t n, int64_t ldb,
+                        double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+    const int64_t rowblocks = (m + 63) / 64;
+    const int64_t nA = rowblocks * L.nchunks, nB = L.n_pad / 4;
+    OZ2_LAUNCH(ev, k_scale, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, k, lda, L.kchunk, rowblocks, nA,
+               (double *)(ws + L.part_s), (int *)(ws + L.part_g), (int *)(ws + L.part_bad), B, n, L.n_pad, ldb, Pp,
+               (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
     return hipGetLastError();
 }
 
-hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s) {
-    hipLaunchKernelGGL(k_row_exponents, dim3(nblk(L.m_pad, 256)), dim3(256), 0, s, (const double *)(ws + L.part_s),
-                       (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad), m, L.m_pad, L.nchunks, Pp,
-                       (int32_t *)(ws + L.e), (int32_t *)(ws + L.ga));
+hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+    OZ2_LAUNCH(ev, k_row_exponents, dim3(nblk(L.m_pad, 256)), dim3(256), 0, s, (const double *)(ws + L.part_s),
+               (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad), m, L.m_pad, L.nchunks, Pp,
+               (int32_t *)(ws + L.e), (int32_t *)(ws + L.ga));
     return hipGetLastError();
 }
 
-hipError_t launch_col_exponents(const double *B, int64_t k, int64_t n, int64_t ldb, double Pp, const Layout &L,
-                                char *ws, hipStream_t s, Ev ev) {
-    OZ2_LAUNCH(ev, k_col_exponents, dim3(nblk(L.n_pad, 4)), dim3(256), 0, s, B, k, n, L.n_pad, ldb, Pp,
-                       (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
-    return hipGetLastError();
-}
-
-hipError_t launch_split(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                        const int32_t *ex, const SplitConsts &sc, int8_t *out, int64_t rows_pad, const Layout &L,
+hipError_t launch_split(const double *A, int64_t m, int64_t lda, const double *B, int64_t n, int64_t ldb, int64_t k,
+                        bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L, char *ws,
                         hipStream_t s, Ev ev) {
-    dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
-    const int64_t plane = rows_pad * L.k_pad;
-    if (k_contiguous)
-        OZ2_LAUNCH(ev, k_split<true>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
-    else
-        OZ2_LAUNCH(ev, k_split<false>, grid, dim3(256), 0, s, X, rows, k, ld, ex, sc, out, plane, L.kb);
+    const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows, tilesK = L.k_pad / kSplitCols;
+    const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
+    const dim3 grid((unsigned)(nA + nB));
+    if (fold_row_exponents) {
+        auto kern = k_split<true>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
+                   (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
+                   L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
+                   L.m_pad * L.k_pad, (int8_t *)(ws + L.rb), L.n_pad * L.k_pad, L.kb);
+    } else {
+        auto kern = k_split<false>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
+                   (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
+                   L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
+                   L.m_pad * L.k_pad, (int8_t *)(ws + L.rb), L.n_pad * L.k_pad, L.kb);
+    }
     return hipGetLastError();
 }
 
