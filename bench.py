@@ -207,6 +207,16 @@ def main():
         ms3 = time_steps(lambda: torch.mm(At, Bt), max(args.steps // 2, 3), 2, torch)
         extras["native_fp64_gemm_tflops"] = round(flops / (ms3 * 1e-3) / 1e12, 3)
         del At, Bt
+        # the vendor INT8 GEMM (torch._int_mm = hipBLASLt) on random int8 of one
+        # modulus' shape, as context for the INT8 roofline fraction
+        try:
+            Ai = torch.randint(-128, 128, (m, k), dtype=torch.int8, device=dev)
+            Bi = torch.randint(-128, 128, (n, k), dtype=torch.int8, device=dev).t()  # column-major k x n
+            ms4 = time_steps(lambda: torch._int_mm(Ai, Bi), max(args.steps, 5), 3, torch)
+            extras["vendor_int8_gemm_tops"] = round(2.0 * m * n * k / (ms4 * 1e-3) / 1e12, 1)
+            del Ai, Bi
+        except Exception as ex:  # pragma: no cover - context only
+            log(f"vendor int8 GEMM not measured: {ex}")
 
     cpu = None
     accuracy = None
