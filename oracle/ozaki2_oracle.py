@@ -42,6 +42,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * log2 is applied only to the significand f in [1, 2) of that sum, and the
     binary exponent is split off exactly, so no rounding depends on it.
   * "cut off" is truncation toward zero.
+  * Single precision ([G] section Zentrale Beiträge names SGEMM): the same
+    steps on the binary32 inputs widened exactly to doubles, and one rounding
+    of X * 2^-(e+f) to binary32 (os2_sgemm, round_to_f32).
   * Accurate mode ([Q] section 2の累乗による整数化, [G] section
     Problemstellung) is read as: bound |A| and |B| from above by 6-bit
     integers on the row/column maxima, form their product with one extra
@@ -472,6 +475,66 @@ def os2_dgemm(A, B, num_moduli: int, mode: str = "fast", e=None, f=None) -> dict
     X = crt(c, tables)
     C = unscale(X, e, f)
     return dict(moduli=moduli, tables=tables, e=e, f=f, RA=RA, RB=RB, Q=Q, c=c, X=X, C=C)
+
+
+# --------------------------------------------------------------------------
+# Single precision ([G] section Zentrale Beiträge: the scheme evaluated for
+# SGEMM as well as DGEMM)
+# --------------------------------------------------------------------------
+# Reading: the same steps on binary32 inputs (every binary32 value is a double,
+# so the exponents, the split and the integer product are those of the FP64
+# path on the widened inputs), and the result is the binary32 value nearest to
+# X * 2^-(e_i + f_j), rounded once, ties to even, subnormals included.
+F32_MANT = 24          # significand bits of binary32
+F32_MIN_EXP = -149     # exponent of the smallest subnormal
+F32_MAX = float(np.finfo(np.float32).max)
+
+
+def round_to_f32(X: int, s: int) -> np.float32:
+    """RN_binary32(X * 2^-s) for an integer X, by integer arithmetic."""
+    if X == 0:
+        return np.float32(0.0)
+    sign = -1 if X < 0 else 1
+    mag = -X if X < 0 else X
+    b = mag.bit_length()
+    # place of the last kept bit, in units of mag: 24 significant bits, but
+    # never below the subnormal quantum 2^-149 (= 2^(s - 149) in units of mag)
+    shift = max(b - F32_MANT, s + F32_MIN_EXP)
+    if shift <= 0:
+        q = mag << -shift
+    else:
+        q, r = divmod(mag, 1 << shift)
+        half = 1 << (shift - 1)
+        if r > half or (r == half and (q & 1)):
+            q += 1
+    v = math.ldexp(float(q), shift - s)  # q < 2^25: exact as a double
+    if v > F32_MAX:
+        return np.float32(sign * np.inf)
+    return np.float32(sign * v)
+
+
+def unscale_f32(X: np.ndarray, e, f) -> np.ndarray:
+    """C_ij = RN_binary32(X_ij * 2^-(e_i + f_j)); NaN rows/columns as unscale."""
+    m, n = X.shape
+    C = np.empty((m, n), dtype=np.float32)
+    for i in range(m):
+        for j in range(n):
+            if e[i] is None or f[j] is None:
+                C[i, j] = np.float32(np.nan)
+            else:
+                C[i, j] = round_to_f32(int(X[i, j]), e[i] + f[j])
+    return C
+
+
+def os2_sgemm(A, B, num_moduli: int, mode: str = "fast", e=None, f=None) -> dict:
+    """The emulation for binary32 A (m, k) and B (k, n): os2_dgemm's steps on
+    the exactly widened inputs, then one rounding to binary32."""
+    A = np.asarray(A, dtype=np.float32)
+    B = np.asarray(B, dtype=np.float32)
+    r = os2_dgemm(A.astype(np.float64), B.astype(np.float64), num_moduli, mode, e=e, f=f)
+    r["C64"] = r["C"]
+    r["C"] = unscale_f32(r["X"], r["e"], r["f"])
+    return r
 
 
 def exact_scaled_product(A, B, e, f) -> np.ndarray:

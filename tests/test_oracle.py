@@ -377,3 +377,73 @@ def test_planted_exponent_error_is_detected():
     assert np.all(2 * np.abs(Y) > r["tables"]["P"] - 1)
     assert not np.any(r["X"] == Y)
     assert not np.any(r["C"] == k)
+
+
+# --------------------------------------------------------------------------
+# Single precision: one rounding of X * 2^-s to binary32
+# --------------------------------------------------------------------------
+def test_round_to_f32_against_exact_doubles():
+    # when X * 2^-s is exactly a double (|X| < 2^53, no double underflow), the
+    # binary32 rounding of that double is the single rounding we want
+    rng = np.random.default_rng(11)
+    for _ in range(4000):
+        X = int(rng.integers(-(2 ** 53) + 1, 2 ** 53))
+        s = int(rng.integers(-100, 221))
+        want = np.float32(np.ldexp(np.float64(X), -s))
+        got = O.round_to_f32(X, s)
+        assert np.float32(got).view(np.uint32) == want.view(np.uint32), (X, s)
+
+
+def test_round_to_f32_ties_subnormals_overflow():
+    r = O.round_to_f32
+    assert r(2 ** 24 + 1, 0) == 2.0 ** 24            # tie to even (down)
+    assert r(2 ** 24 + 3, 0) == 2.0 ** 24 + 4        # tie to even (up)
+    assert r(2 ** 60 + 2 ** 36, 0) == 2.0 ** 60      # tie far above 2^53, to even
+    assert r(2 ** 60 + 2 ** 36 + 1, 0) == 2.0 ** 60 + 2 ** 37  # just above the tie
+    tiny = np.float32(2.0 ** -149)
+    assert r(1, 149) == tiny and r(1, 150) == 0.0    # 2^-150 ties to the even zero
+    assert r(3, 151) == tiny                         # 0.75 quantum rounds up
+    assert r(3, 150) == np.float32(2.0 ** -148)      # 1.5 quanta tie to 2 quanta
+    assert r(2 ** 200 + 1, 200 + 126 + 23) == tiny * np.float32(2.0 ** 0)  # huge X, deep subnormal
+    big = float(np.finfo(np.float32).max)            # (2 - 2^-23) * 2^127
+    assert r(int(big), 0) == np.float32(big)
+    assert r(int(big) + 2 ** 103, 0) == np.float32(np.inf)  # tie above max rounds to even = inf
+    assert r(int(big) + 2 ** 103 - 1, 0) == np.float32(big)
+    assert r(-(2 ** 24 + 1), 0) == -(2.0 ** 24) and r(0, 5) == 0.0
+
+
+def test_sgemm_small_integers_and_nonfinite():
+    rng = np.random.default_rng(2)
+    A = rng.integers(-3, 4, (20, 30)).astype(np.float32)
+    B = rng.integers(-3, 4, (30, 9)).astype(np.float32)
+    A[4] = 0.0
+    A[7, 3] = np.inf
+    r = O.os2_sgemm(A, B, 8)
+    C = r["C"]
+    assert C.dtype == np.float32
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    ok = np.ones(20, bool)
+    ok[7] = False
+    assert np.array_equal(C[ok], exact[ok].astype(np.float32))
+    assert np.all(np.isnan(C[7])) and np.all(C[4] == 0.0)
+    # the binary32 result is the double result of the same X rounded once more
+    # only where that cannot double-round: here all values are small integers
+    assert np.array_equal(C[ok], r["C64"][ok].astype(np.float32))
+
+
+def test_sgemm_accuracy_against_native_fp32():
+    # [G] Zentrale Beiträge: the scheme is evaluated for SGEMM; with 8 moduli it
+    # is at least as accurate as native binary32 on moderately spread data,
+    # and 9 moduli are needed for the wider spread
+    rng = np.random.default_rng(5)
+    n = 160
+    for phi, N in ((0.5, 8), (1.0, 8), (2.0, 9)):
+        A = ((rng.random((n, n)) - 0.5) * np.exp(phi * rng.standard_normal((n, n)))).astype(np.float32)
+        B = ((rng.random((n, n)) - 0.5) * np.exp(phi * rng.standard_normal((n, n)))).astype(np.float32)
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        ref = A64 @ B64
+        scale = np.abs(A64) @ np.abs(B64)
+        ecw = lambda C: float(np.max(np.abs(C.astype(np.float64) - ref) / scale))
+        assert ecw(O.os2_sgemm(A, B, N)["C"]) <= ecw(A @ B), (phi, N)
+        # and never worse than the final binary32 rounding allows
+        assert ecw(O.os2_sgemm(A, B, 10)["C"]) <= 2.0 ** -24
