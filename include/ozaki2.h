@@ -164,6 +164,33 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
                      const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
                      void *stream);
 
+/*
+ * Single precision: C := A * B for binary32 A, B, C, emulated by the same
+ * steps ([G] section Zentrale Beiträge: the scheme is evaluated for SGEMM as
+ * well as DGEMM). The binary32 inputs are widened exactly to doubles, so the
+ * exponents, residues and integer products are those ozaki2_dgemm computes
+ * for the widened operands; each entry of C is X * 2^-(e_i + f_j) rounded
+ * once to binary32 (to nearest, ties to even, subnormals included). 8 moduli
+ * give about the accuracy of native binary32 on typical data.
+ * Arguments, layouts, status codes and workspace sizes are exactly those of
+ * ozaki2_dgemm / ozaki2_dgemm_ws / ozaki2_dgemm_debug (ozaki2_workspace_size
+ * and ozaki2_debug_workspace_size apply unchanged), with float in place of
+ * double for A, B and C.
+ */
+int ozaki2_sgemm(int64_t m, int64_t n, int64_t k,
+                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int num_moduli, int mode, void *stream);
+int ozaki2_sgemm_ws(int64_t m, int64_t n, int64_t k,
+                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float *C, int64_t ldc, int num_moduli, int mode,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k,
+                       const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc, int num_moduli, int mode,
+                       void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
+                       int32_t *prod_out, uint8_t *red_out, void *stream);
+
 /* Workspace bytes for ozaki2_dgemm_debug (larger: raw int32 products). */
 size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
 

@@ -27,7 +27,7 @@ EXPORTS = (
     "ozaki2_dgemm", "ozaki2_workspace_size", "ozaki2_dgemm_ws", "ozaki2_dgemm_debug",
     "ozaki2_debug_workspace_size", "ozaki2_max_moduli", "ozaki2_moduli", "ozaki2_scaling_constant",
     "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
-    "ozaki2_finalize", "ozaki2_crt_debug",
+    "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
 )
 
 _lib = None
@@ -59,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_dgemm_ws.restype = i32
     L.ozaki2_dgemm_debug.argtypes = prod + [p, sz, p, p, p, p, p, p, p]
     L.ozaki2_dgemm_debug.restype = i32
+    for name in ("ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug"):
+        twin = getattr(L, name.replace("sgemm", "dgemm"))
+        getattr(L, name).argtypes = twin.argtypes
+        getattr(L, name).restype = i32
     L.ozaki2_crt_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, sz, p]
     L.ozaki2_crt_debug.restype = i32
     L.ozaki2_max_moduli.argtypes = []
@@ -103,6 +107,21 @@ def ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, worksp
                        e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
     return lib().ozaki2_dgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace,
                                     workspace_bytes, e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_sgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) -> int:
+    return lib().ozaki2_sgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_sgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_sgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                 stream)
+
+
+def ozaki2_sgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                       e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
+    return lib().ozaki2_sgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                    e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
 
 
 def ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream=0) -> int:
@@ -171,26 +190,36 @@ def dgemm(A, B, num_moduli: int = 16, mode="fast", out=None, workspace=None):
     Row-major C = A B is column-major C^T = B^T A^T, so the library is called
     with the operands swapped; the scaling is symmetric in the two operands.
     """
+    return _gemm(A, B, num_moduli, mode, out, workspace, single=False)
+
+
+def sgemm(A, B, num_moduli: int = 8, mode="fast", out=None, workspace=None):
+    """C = A @ B for float32 CUDA (HIP) tensors (ozaki2_sgemm), as dgemm."""
+    return _gemm(A, B, num_moduli, mode, out, workspace, single=True)
+
+
+def _gemm(A, B, num_moduli, mode, out, workspace, single):
     import torch
 
-    if A.dtype != torch.float64 or B.dtype != torch.float64 or not A.is_cuda or not B.is_cuda:
-        raise TypeError("A and B must be float64 tensors on the GPU")
+    dt = torch.float32 if single else torch.float64
+    if A.dtype != dt or B.dtype != dt or not A.is_cuda or not B.is_cuda:
+        raise TypeError(f"A and B must be {dt} tensors on the GPU")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError("shapes do not multiply")
     A = A.contiguous()
     B = B.contiguous()
     m, k = A.shape
     n = B.shape[1]
-    C = out if out is not None else torch.empty((m, n), dtype=torch.float64, device=A.device)
+    C = out if out is not None else torch.empty((m, n), dtype=dt, device=A.device)
     stream = torch.cuda.current_stream(A.device).cuda_stream
     md = _mode(mode)
+    plain, ws_form = (ozaki2_sgemm, ozaki2_sgemm_ws) if single else (ozaki2_dgemm, ozaki2_dgemm_ws)
     if workspace is None:
-        st = ozaki2_dgemm(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
-                          num_moduli, md, stream)
+        st = plain(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                   num_moduli, md, stream)
     else:
-        st = ozaki2_dgemm_ws(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
-                             num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             stream)
+        st = ws_form(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                     num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     if st:
-        raise Ozaki2Error(st, "ozaki2_dgemm")
+        raise Ozaki2Error(st, "ozaki2_sgemm" if single else "ozaki2_dgemm")
     return C

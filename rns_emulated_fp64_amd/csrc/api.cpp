@@ -25,8 +25,8 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 int64_t round_up(int64_t v, int64_t g) { return (v + g - 1) / g * g; }
 
 // Checks in signature order; returns 0 or -(index of the first bad argument).
-int validate(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
-             const double *C, int64_t ldc, int nmod, int mode) {
+int validate(int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
+             const void *C, int64_t ldc, int nmod, int mode) {
     if (m < 0) return -1;
     if (n < 0) return -2;
     if (k < 0) return -3;
@@ -147,7 +147,7 @@ struct DebugOut {
     uint8_t *red;
 };
 
-int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb, double *C,
+int run(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
         int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
     const Tables *T = get_tables(nmod);
     // Timing events (start/stop per phase) are recorded before the first and
@@ -177,14 +177,14 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
 
     // Step 1: squared norms of the rows of A and exponents of the columns of
     // B ([G] Methodik), one launch.
-    HIP_TRY(launch_scale(A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
+    HIP_TRY(launch_scale(el, A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
     if (accurate) {
         // Accurate mode bounds the products with one extra INT8 GEMM first
         // ([G] Problemstellung).
         HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
-        HIP_TRY(launch_quantize(A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
+        HIP_TRY(launch_quantize(el, A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
                                 L.m_pad, L, s));
-        HIP_TRY(launch_quantize(B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
+        HIP_TRY(launch_quantize(el, B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
                                 L.n_pad, L, s));
         HIP_TRY(launch_fill_i32((int32_t *)(ws + L.rowmax), L.m_pad, 0, s));
         HIP_TRY(launch_fill_i32((int32_t *)(ws + L.colmax), L.n_pad, 0, s));
@@ -195,7 +195,7 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
 
     // Steps 1 + 2: integerize and split both operands into residues, one
     // launch (in fast mode it also finishes the row exponents of A).
-    HIP_TRY(launch_split(A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
+    HIP_TRY(launch_split(el, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
                          ev_of(kPhaseSplit, true, true)));
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
 
@@ -204,7 +204,7 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
                             (int8_t *)(ws + L.planes), L, s, ev_of(kPhaseGemm, true, true)));
 
     // Steps 4 + 5: reconstruction and unscaling.
-    HIP_TRY(launch_crt((const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
+    HIP_TRY(launch_crt(el, (const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
                        ev_of(kPhaseCrt, true, true)));
 
     if (dbg) {
@@ -226,9 +226,9 @@ int run(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const dou
 }
 
 // Common front end of the product entry points.
-int front(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb, double *C,
-          int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, bool use_cache, const DebugOut *dbg,
-          void *stream) {
+int front(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
+          void *C, int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, bool use_cache,
+          const DebugOut *dbg, void *stream) {
     int st = validate(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode);
     if (st) return st;
     if (!layout_fits(m, n, k, mode)) return OZAKI2_ERR_UNSUPPORTED;
@@ -236,14 +236,14 @@ int front(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const d
     hipStream_t s = (hipStream_t)stream;
     if (m == 0 || n == 0) return OZAKI2_SUCCESS;
     if (k == 0) {
-        HIP_TRY(launch_zero_fill(C, m, n, ldc, s));
+        HIP_TRY(launch_zero_fill(el, C, m, n, ldc, s));
         return OZAKI2_SUCCESS;
     }
     const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr);
     if (!use_cache) {
         if (workspace == nullptr) return -12;
         if (wbytes < L.total) return OZAKI2_ERR_WORKSPACE;
-        return run(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
+        return run(el, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
     }
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -264,7 +264,7 @@ int front(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const d
         g_cache.ptr[dev] = p;
         g_cache.bytes[dev] = L.total;
     }
-    return run(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
+    return run(el, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
 }
 
 }  // namespace
@@ -276,7 +276,7 @@ extern "C" {
 
 int ozaki2_dgemm(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
                  double *C, int64_t ldc, int num_moduli, int mode, void *stream) {
-    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
+    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
 }
 
 size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode) {
@@ -298,8 +298,8 @@ size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_modu
 int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
                     double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                     void *stream) {
-    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, nullptr,
-                 stream);
+    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false,
+                 nullptr, stream);
 }
 
 int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
@@ -307,7 +307,29 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
     DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
-    return front(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d, stream);
+    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d,
+                 stream);
+}
+
+int ozaki2_sgemm(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int num_moduli, int mode, void *stream) {
+    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
+}
+
+int ozaki2_sgemm_ws(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false,
+                 nullptr, stream);
+}
+
+int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
+                       uint8_t *red_out, void *stream) {
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d,
+                 stream);
 }
 
 int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
@@ -331,7 +353,7 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
     hipStream_t s = (hipStream_t)stream;
     int8_t *planes = (int8_t *)((char *)workspace + L.planes);
     HIP_TRY(launch_pack_planes(residues, num_moduli, T->mod, m, n, L, planes, s));
-    HIP_TRY(launch_crt(planes, m, n, e, f, T->crt, C, ldc, L, s));
+    HIP_TRY(launch_crt(Elem::f64, planes, m, n, e, f, T->crt, C, ldc, L, s));
     return OZAKI2_SUCCESS;
 }
 

@@ -81,14 +81,17 @@ struct Ev {
     hipEvent_t stop = nullptr;
 };
 
+// Element type of A, B and C: FP64 (ozaki2_dgemm) or binary32 (ozaki2_sgemm).
+enum class Elem { f64, f32 };
+
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
-hipError_t launch_scale(const double *A, int64_t m, int64_t k, int64_t lda, const double *B, int64_t n,
+hipError_t launch_scale(Elem el, const void *A, int64_t m, int64_t k, int64_t lda, const void *B, int64_t n,
                         int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_split(const double *A, int64_t m, int64_t lda, const double *B, int64_t n, int64_t ldb,
+hipError_t launch_split(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
                         int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L,
                         char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+hipError_t launch_quantize(Elem el, const void *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                            const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
                            hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
@@ -100,9 +103,9 @@ hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *ro
                              const Layout &L, hipStream_t s);
 hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layout &L, char *ws,
                                      hipStream_t s, Ev ev = {});
-hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
-                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev = {});
-hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
+hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+                      const CrtConsts &cc, void *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev = {});
+hipError_t launch_zero_fill(Elem el, void *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
 hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
 hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,

@@ -84,7 +84,8 @@ __device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
 // each thread accumulates every 4th column of its chunk, and the 4 lanes of a
 // row are merged in a fixed order through LDS. Output: one partial
 // (s, g, nonfinite) per (chunk, row).
-__device__ __forceinline__ void row_norms_block(const double *__restrict__ A, int64_t m, int64_t k, int64_t lda,
+template <class T>
+__device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                 int64_t kchunk, double *__restrict__ ps, int *__restrict__ pg,
                                                 int *__restrict__ pbad, int64_t rowblock, int64_t chunk) {
     __shared__ double sh_s[4][64];
@@ -98,12 +99,12 @@ __device__ __forceinline__ void row_norms_block(const double *__restrict__ A, in
     int g = kExpEmpty;
     int bad = 0;
     if (i < m) {
-        const double *a = A + i;
+        const T *a = A + i;
         int64_t h = h0 + kl;
         for (; h + 28 < h1; h += 32) {
             double v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = a[(h + 4 * u) * lda];
+            for (int u = 0; u < 8; ++u) v[u] = (double)a[(h + 4 * u) * lda];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 double x = fabs(v[u]);
@@ -112,7 +113,7 @@ __device__ __forceinline__ void row_norms_block(const double *__restrict__ A, in
             }
         }
         for (; h < h1; h += 4) {
-            double x = fabs(a[h * lda]);
+            double x = fabs((double)a[h * lda]);
             if (!(x <= DBL_MAX)) bad = 1;
             else ssq_add(s, g, x);
         }
@@ -192,7 +193,8 @@ __global__ __launch_bounds__(256) void k_row_exponents(const double *__restrict_
 // Columns of column-major B (contiguous): one wavefront per column, lanes
 // stride the column, then a fixed xor-butterfly merge (every lane ends with
 // the same bits).
-__device__ __forceinline__ void col_exponents_block(const double *__restrict__ B, int64_t k, int64_t n,
+template <class T>
+__device__ __forceinline__ void col_exponents_block(const T *__restrict__ B, int64_t k, int64_t n,
                                                     int64_t n_pad, int64_t ldb, double Pp, int32_t *__restrict__ f,
                                                     int32_t *__restrict__ gb, int64_t blk) {
     const int lane = threadIdx.x & 63;
@@ -205,7 +207,7 @@ __device__ __forceinline__ void col_exponents_block(const double *__restrict__ B
         }
         return;
     }
-    const double *col = B + j * ldb;
+    const T *col = B + j * ldb;
     double s = 0.0;
     int g = kExpEmpty;
     int bad = 0;
@@ -213,7 +215,7 @@ __device__ __forceinline__ void col_exponents_block(const double *__restrict__ B
     for (; h + 7 * 64 < k; h += 8 * 64) {
         double v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = col[h + 64 * u];
+        for (int u = 0; u < 8; ++u) v[u] = (double)col[h + 64 * u];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             double x = fabs(v[u]);
@@ -222,7 +224,7 @@ __device__ __forceinline__ void col_exponents_block(const double *__restrict__ B
         }
     }
     for (; h < k; h += 64) {
-        double x = fabs(col[h]);
+        double x = fabs((double)col[h]);
         if (!(x <= DBL_MAX)) bad = 1;
         else ssq_add(s, g, x);
     }
@@ -251,10 +253,11 @@ __device__ __forceinline__ void col_exponents_block(const double *__restrict__ B
 
 // Step 1 for both operands in one launch: blocks [0, nA) are row-norm blocks
 // of A (row block fastest, then k-chunk), the rest column blocks of B.
-__global__ __launch_bounds__(256) void k_scale(const double *__restrict__ A, int64_t m, int64_t k, int64_t lda,
+template <class T>
+__global__ __launch_bounds__(256) void k_scale(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                int64_t kchunk, int64_t rowblocks, int64_t nA,
                                                double *__restrict__ ps, int *__restrict__ pg,
-                                               int *__restrict__ pbad, const double *__restrict__ B, int64_t n,
+                                               int *__restrict__ pbad, const T *__restrict__ B, int64_t n,
                                                int64_t n_pad, int64_t ldb, double Pp, int32_t *__restrict__ f,
                                                int32_t *__restrict__ gb) {
     const int64_t bid = blockIdx.x;
@@ -301,8 +304,8 @@ __global__ __launch_bounds__(256) void k_accurate_exponents(const int32_t *__res
 // the 16 bytes lane (t%64) holds in the packed layout.
 constexpr int kSplitRows = 32, kSplitCols = 128, kSplitLd = kSplitCols + 2;
 
-template <bool KCONTIG>
-__device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const double *__restrict__ X,
+template <bool KCONTIG, class T>
+__device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const T *__restrict__ X,
                                                 int64_t rows, int64_t kdim, int64_t ld, int64_t r0,
                                                 int64_t h0) {
     // All 16 loads of a thread are issued before any LDS write; out-of-range
@@ -318,7 +321,7 @@ __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const 
         for (int it = 0; it < 16; ++it) {
             const int64_t h = h0 + hh + 8 * it;
             const bool ok = rok && h < kdim;
-            const double x = X[rc + (ok ? h : 0) * ld];
+            const double x = (double)X[rc + (ok ? h : 0) * ld];
             v[it] = ok ? x : 0.0;
         }
 #pragma unroll
@@ -331,8 +334,8 @@ __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const 
             const int64_t r = r0 + rq + 4 * it;
             const bool rok = r < rows;
             const bool ok0 = rok && h < kdim, ok1 = rok && h + 1 < kdim;
-            const double *row = X + (rok ? r : 0) * ld;
-            const double x0 = row[ok0 ? h : 0], x1 = row[ok1 ? h + 1 : 0];
+            const T *row = X + (rok ? r : 0) * ld;
+            const double x0 = (double)row[ok0 ? h : 0], x1 = (double)row[ok1 ? h + 1 : 0];
             v[2 * it] = ok0 ? x0 : 0.0;
             v[2 * it + 1] = ok1 ? x1 : 0.0;
         }
@@ -356,13 +359,13 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
 
 // One split block: rows [bx*32, +32) x K [by*128, +128) of X (KCONTIG: K
 // runs along memory). ex_row(rr) gives the exponent of row bx*32 + rr.
-template <bool KCONTIG, class ExpOf>
-__device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const double *__restrict__ X, int64_t rows,
+template <bool KCONTIG, class T, class ExpOf>
+__device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *__restrict__ X, int64_t rows,
                                             int64_t kdim, int64_t ld, ExpOf ex_row, const SplitConsts &sc,
                                             int8_t *__restrict__ out, int64_t plane_bytes, int64_t kb, int64_t bx,
                                             int64_t by) {
     const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
-    split_load_tile<KCONTIG>(tile, X, rows, kdim, ld, r0, h0);
+    split_load_tile<KCONTIG, T>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
 
     const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
@@ -421,9 +424,9 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const doub
 // exponents of A's rows are merged here from the row-norm partials (the first
 // K tile of each row tile also stores them for the reconstruction); otherwise
 // they are read from e.
-template <bool FOLD>
-__global__ __launch_bounds__(256) void k_split(const double *__restrict__ A, int64_t m, int64_t lda,
-                                               const double *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
+template <bool FOLD, class T>
+__global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t m, int64_t lda,
+                                               const T *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
                                                int64_t tilesA, int64_t tilesB, int64_t nA,
                                                const double *__restrict__ ps,
                                                const int *__restrict__ pg, const int *__restrict__ pbad,
@@ -445,28 +448,28 @@ __global__ __launch_bounds__(256) void k_split(const double *__restrict__ A, int
                 if (by == 0) e[i] = ev;  // i < m_pad: the workspace holds m_pad entries
             }
             // split_block's barrier after the tile load orders these LDS writes
-            split_block<false>(tile, A, m, kdim, lda, [&](int rr) { return sh_e[rr]; }, sc, RA, planeA, kb, bx, by);
+            split_block<false, T>(tile, A, m, kdim, lda, [&](int rr) { return sh_e[rr]; }, sc, RA, planeA, kb, bx, by);
         } else {
             const int32_t *er = e + bx * kSplitRows;
-            split_block<false>(tile, A, m, kdim, lda, [&](int rr) { return (int)er[rr]; }, sc, RA, planeA, kb, bx,
+            split_block<false, T>(tile, A, m, kdim, lda, [&](int rr) { return (int)er[rr]; }, sc, RA, planeA, kb, bx,
                                by);
         }
     } else {
         const int64_t b = bid - nA;
         const int64_t bx = b % tilesB, by = b / tilesB;
         const int32_t *fr = f + bx * kSplitRows;
-        split_block<true>(tile, B, n, kdim, ldb, [&](int rr) { return (int)fr[rr]; }, sc, RB, planeB, kb, bx, by);
+        split_block<true, T>(tile, B, n, kdim, ldb, [&](int rr) { return (int)fr[rr]; }, sc, RB, planeB, kb, bx, by);
     }
 }
 
 // Accurate mode: Abar_ih = ceil(|a_ih| * 2^(6 - r_i)) in [0, 64], same packing.
-template <bool KCONTIG>
-__global__ __launch_bounds__(256) void k_quantize(const double *__restrict__ X, int64_t rows, int64_t kdim,
+template <bool KCONTIG, class T>
+__global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ X, int64_t rows, int64_t kdim,
                                                   int64_t ld, const int32_t *__restrict__ gx,
                                                   int8_t *__restrict__ out, int64_t kb) {
     __shared__ double tile[kSplitRows][kSplitLd];
     const int64_t r0 = (int64_t)blockIdx.x * kSplitRows, h0 = (int64_t)blockIdx.y * kSplitCols;
-    split_load_tile<KCONTIG>(tile, X, rows, kdim, ld, r0, h0);
+    split_load_tile<KCONTIG, T>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
     const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
     const int kk0 = fb * 32 + 16 * (lane >> 5);
@@ -833,10 +836,13 @@ __device__ __forceinline__ uint64_t small_int_bits(double x) {
     return (uint64_t)__double_as_longlong(x + 0x1p52) & ((1ull << 52) - 1);
 }
 
-// RN(x) * 2^-scale_down for a normalized non-negative 40-bit piece vector
-// (x[0..2] in [0, 2^40), x[3] in [0, 2^36)), rounded to nearest-even from the
-// exact 160-bit integer.
-__device__ __forceinline__ double limbs_to_double_rn(const double x[4], int scale_down) {
+// |X| * 2^-scale_down for a normalized non-negative 40-bit piece vector
+// (x[0..2] in [0, 2^40), x[3] in [0, 2^36)), from the exact 160-bit integer:
+// rounded to nearest-even (ODD = false), or to 53 bits with the bits below
+// OR-ed into the last place (round to odd, ODD = true), which a later rounding
+// to binary32 turns into the single rounding of the whole integer.
+template <bool ODD>
+__device__ __forceinline__ double limbs_to_double(const double x[4], int scale_down) {
     const uint64_t L0 = small_int_bits(x[0]), L1 = small_int_bits(x[1]), L2 = small_int_bits(x[2]),
                    L3 = small_int_bits(x[3]);
     const uint64_t w0 = L0 | (L1 << 40);
@@ -858,50 +864,75 @@ __device__ __forceinline__ double limbs_to_double_rn(const double x[4], int scal
     const bool sticky = ((lz ? (nxt << lz) : nxt) | low) != 0;
     uint64_t mant = hi >> 11;
     const uint64_t rb = hi & 0x7ff;
-    mant += (rb > 0x400 || (rb == 0x400 && (sticky || (mant & 1)))) ? 1 : 0;
+    if (ODD)
+        mant |= (rb != 0 || sticky) ? 1 : 0;
+    else
+        mant += (rb > 0x400 || (rb == 0x400 && (sticky || (mant & 1)))) ? 1 : 0;
     return ldexp((double)mant, scale - lz + 11 - scale_down);
 }
 
-// RN(x) * 2^-scale_down for a normalized non-negative 32-bit piece vector
-// (x[t] in [0, 2^32)): the top 64 bits of the 128-bit integer, with the bits
-// below OR-ed into the last place (round to odd), convert to double with a
-// single rounding, which then equals the rounding of the whole integer
-// (64 >= 53 + 2 bits).
-__device__ __forceinline__ double limbs32_to_double_rn(const double x[4], int scale_down) {
+// The same for a normalized non-negative 32-bit piece vector (x[t] in
+// [0, 2^32)): the top 64 bits of the 128-bit integer with the bits below
+// OR-ed into the last place (round to odd) convert to double with a single
+// rounding, which then equals the rounding of the whole integer (64 >= 53 + 2
+// bits); with ODD the 64 bits are rounded to odd at 53 bits instead.
+template <bool ODD>
+__device__ __forceinline__ double limbs32_to_double(const double x[4], int scale_down) {
     const uint64_t w0 = ((uint64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
     const uint64_t w1 = ((uint64_t)(uint32_t)x[3] << 32) | (uint32_t)x[2];
-    if (w1 == 0) return ldexp((double)w0, -scale_down);
-    const int lz = __clzll(w1);
-    const uint64_t top = (w1 << lz) | ((w0 >> 1) >> (63 - lz));
-    const uint64_t odd = (w0 << lz) != 0 ? 1 : 0;
-    return ldexp((double)(top | odd), 64 - lz - scale_down);
+    uint64_t top;
+    int scale;
+    bool odd;
+    if (w1 != 0) {
+        const int lz = __clzll(w1);
+        top = (w1 << lz) | ((w0 >> 1) >> (63 - lz));
+        odd = (w0 << lz) != 0;
+        scale = 64 - lz;
+    } else {
+        if (!ODD) return ldexp((double)w0, -scale_down);
+        if (w0 == 0) return 0.0;
+        const int lz = __clzll(w0);
+        top = w0 << lz;
+        odd = false;
+        scale = -lz;
+    }
+    if (!ODD) return ldexp((double)(top | (odd ? 1 : 0)), scale - scale_down);
+    const uint64_t mant = (top >> 11) | (((top & 0x7ff) != 0 || odd) ? 1 : 0);
+    return ldexp((double)mant, scale + 11 - scale_down);
 }
 
-__device__ __forceinline__ double crt_finish(const double S[4], int ei, int fj, const CrtConsts &cc) {
+// C value of type OutT: RN(X) * 2^-(e + f) for double, the single binary32
+// rounding of X * 2^-(e + f) for float (round to odd at 53 bits, an exact
+// power-of-two scaling, then one rounding to binary32); NaN for a non-finite
+// row or column.
+template <class OutT>
+__device__ __forceinline__ OutT crt_finish(const double S[4], int ei, int fj, const CrtConsts &cc) {
     // S / 2^120 (|S/P| < 2^12)
     const double s120 = fma(S[0], 0x1p-120, fma(S[1], 0x1p-80, fma(S[2], 0x1p-40, S[3])));
     double x[4], sg;
     crt_lift<40>(S, x, sg, s120, cc.P, cc.H, cc.pinv120);
-    const double mag = limbs_to_double_rn(x, ei + fj);
-    return (ei == kExpNonfinite || fj == kExpNonfinite) ? __builtin_nan("") : sg * mag;
+    const double mag = limbs_to_double<sizeof(OutT) == 4>(x, ei + fj);
+    return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
 
 // As crt_finish for S in 32-bit pieces (P < 2^128, at most 16 moduli).
-__device__ __forceinline__ double crt_finish32(const double S[4], int ei, int fj, const CrtConsts &cc) {
+template <class OutT>
+__device__ __forceinline__ OutT crt_finish32(const double S[4], int ei, int fj, const CrtConsts &cc) {
     const double s96 = fma(S[0], 0x1p-96, fma(S[1], 0x1p-64, fma(S[2], 0x1p-32, S[3])));
     double x[4], sg;
     crt_lift<32>(S, x, sg, s96, cc.P32, cc.H32, cc.pinv96);
-    const double mag = limbs32_to_double_rn(x, ei + fj);
-    return (ei == kExpNonfinite || fj == kExpNonfinite) ? __builtin_nan("") : sg * mag;
+    const double mag = limbs32_to_double<sizeof(OutT) == 4>(x, ei + fj);
+    return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
 
 // One thread per 4 consecutive rows of one column. The loop over the moduli is
 // kept rolled (one plane load per trip): on MI355X this overlaps the plane
 // traffic with the arithmetic better than hoisting all loads.
 constexpr int kCrtRows = 4;
+template <class OutT>
 __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, int64_t plane_elems,
                                              int64_t m_pad, int64_t m, int64_t n, const int32_t *__restrict__ e,
-                                             const int32_t *__restrict__ f, CrtConsts cc, double *__restrict__ C,
+                                             const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C,
                                              int64_t ldc) {
     const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kCrtRows;
     if (i0 >= m) return;
@@ -929,7 +960,7 @@ __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, 
 #pragma unroll
         for (int u = 0; u < kCrtRows; ++u) {
             const int64_t i = i0 + u;
-            if (i < m) C[i + j * ldc] = crt_finish(S[u], e[i], fj, cc);
+            if (i < m) C[i + j * ldc] = crt_finish<OutT>(S[u], e[i], fj, cc);
         }
     }
 }
@@ -945,10 +976,10 @@ __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, 
 // even) matches that k-half, so lane L gets back exactly the 16 digit sums of
 // its own entry, digit v in register v. S is then assembled from the D_v into
 // four exact 32-bit pieces (|piece| < 2^42.1) for crt_finish32.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_crt_mma(const int8_t *__restrict__ planes, int64_t plane_elems,
-                                                 int64_t m_pad, int64_t m, int64_t n,
-                                                 const int32_t *__restrict__ e, const int32_t *__restrict__ f,
-                                                 CrtConsts cc, double *__restrict__ C, int64_t ldc) {
+template <class OutT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_crt_mma(
+    const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
+    const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
     __shared__ __attribute__((aligned(16))) int8_t digit[16][16];
     if (threadIdx.x < 64) {
         const int v = threadIdx.x >> 2, b4 = (threadIdx.x & 3) * 4;
@@ -996,7 +1027,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
                 S[t] = fma((double)hi, 65536.0, (double)lo);
             }
             const int64_t i = i0 + u;
-            if (i < m) C[i + j * ldc] = crt_finish32(S, e[i], fj, cc);
+            if (i < m) C[i + j * ldc] = crt_finish32<OutT>(S, e[i], fj, cc);
         }
     }
 }
@@ -1009,10 +1040,11 @@ __global__ void k_fill_i32(int32_t *p, int64_t count, int32_t v) {
     if (i < count) p[i] = v;
 }
 
-__global__ void k_zero_c(double *C, int64_t m, int64_t n, int64_t ldc) {
+template <class T>
+__global__ void k_zero_c(T *C, int64_t m, int64_t n, int64_t ldc) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= m) return;
-    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) C[i + j * ldc] = 0.0;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) C[i + j * ldc] = (T)0;
 }
 
 // packed [l][rows_pad/32][kb][64][16] -> logical [l][rows][k]
@@ -1071,14 +1103,23 @@ __global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t 
 static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count + per - 1) / per); }
 static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
 
-hipError_t launch_scale(const double *A, int64_t m, int64_t k, int64_t lda, const double *B, int64_t n, int64_t ldb,
-                        double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+template <class T>
+static hipError_t launch_scale_t(const T *A, int64_t m, int64_t k, int64_t lda, const T *B, int64_t n, int64_t ldb,
+                                 double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t rowblocks = (m + 63) / 64;
     const int64_t nA = rowblocks * L.nchunks, nB = L.n_pad / 4;
-    OZ2_LAUNCH(ev, k_scale, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, k, lda, L.kchunk, rowblocks, nA,
+    auto kern = k_scale<T>;
+    OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, k, lda, L.kchunk, rowblocks, nA,
                (double *)(ws + L.part_s), (int *)(ws + L.part_g), (int *)(ws + L.part_bad), B, n, L.n_pad, ldb, Pp,
                (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
     return hipGetLastError();
+}
+
+hipError_t launch_scale(Elem el, const void *A, int64_t m, int64_t k, int64_t lda, const void *B, int64_t n,
+                        int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+    if (el == Elem::f32)
+        return launch_scale_t((const float *)A, m, k, lda, (const float *)B, n, ldb, Pp, L, ws, s, ev);
+    return launch_scale_t((const double *)A, m, k, lda, (const double *)B, n, ldb, Pp, L, ws, s, ev);
 }
 
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
@@ -1088,36 +1129,49 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
     return hipGetLastError();
 }
 
-hipError_t launch_split(const double *A, int64_t m, int64_t lda, const double *B, int64_t n, int64_t ldb, int64_t k,
-                        bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L, char *ws,
-                        hipStream_t s, Ev ev) {
+template <bool FOLD, class T>
+static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B, int64_t n, int64_t ldb, int64_t k,
+                                 double Pp, const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows, tilesK = L.k_pad / kSplitCols;
     const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
-    const dim3 grid((unsigned)(nA + nB));
-    if (fold_row_exponents) {
-        auto kern = k_split<true>;
-        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
-                   (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
-                   L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
-                   L.m_pad * L.k_pad, (int8_t *)(ws + L.rb), L.n_pad * L.k_pad, L.kb);
-    } else {
-        auto kern = k_split<false>;
-        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
-                   (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
-                   L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
-                   L.m_pad * L.k_pad, (int8_t *)(ws + L.rb), L.n_pad * L.k_pad, L.kb);
-    }
+    auto kern = k_split<FOLD, T>;
+    OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
+               (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
+               L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
+               L.m_pad * L.k_pad, (int8_t *)(ws + L.rb), L.n_pad * L.k_pad, L.kb);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(const double *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L, hipStream_t s) {
+hipError_t launch_split(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
+                        int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L,
+                        char *ws, hipStream_t s, Ev ev) {
+    if (el == Elem::f32) {
+        const float *a = (const float *)A, *b = (const float *)B;
+        return fold_row_exponents ? launch_split_t<true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
+                                  : launch_split_t<false>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+    }
+    const double *a = (const double *)A, *b = (const double *)B;
+    return fold_row_exponents ? launch_split_t<true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
+                              : launch_split_t<false>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+}
+
+template <class T>
+static hipError_t launch_quantize_t(const T *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                                    const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
+                                    hipStream_t s) {
     dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
     if (k_contiguous)
-        hipLaunchKernelGGL(k_quantize<true>, grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
+        hipLaunchKernelGGL((k_quantize<true, T>), grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
     else
-        hipLaunchKernelGGL(k_quantize<false>, grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
+        hipLaunchKernelGGL((k_quantize<false, T>), grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
     return hipGetLastError();
+}
+
+hipError_t launch_quantize(Elem el, const void *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
+                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L, hipStream_t s) {
+    if (el == Elem::f32)
+        return launch_quantize_t((const float *)X, rows, k, ld, k_contiguous, gx, out, rows_pad, L, s);
+    return launch_quantize_t((const double *)X, rows, k, ld, k_contiguous, gx, out, rows_pad, L, s);
 }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s) {
@@ -1186,17 +1240,26 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
     return hipGetLastError();
 }
 
-hipError_t launch_crt(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
-                      const CrtConsts &cc, double *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
+template <class OutT>
+static hipError_t launch_crt_t(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+                               const CrtConsts &cc, OutT *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
     dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
     if (cc.n <= 16 && cc.nd <= 16) {
-        OZ2_LAUNCH(ev, k_crt_mma, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+        auto kern = k_crt_mma<OutT>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     } else {
         // 17..20 moduli: the 2 x 2 MFMA blocks are mostly padding there, and
         // the FMA form measures slightly faster on MI355X
-        OZ2_LAUNCH(ev, k_crt, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+        auto kern = k_crt<OutT>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
+                      const CrtConsts &cc, void *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
+    if (el == Elem::f32) return launch_crt_t(planes, m, n, e, f, cc, (float *)C, ldc, L, s, ev);
+    return launch_crt_t(planes, m, n, e, f, cc, (double *)C, ldc, L, s, ev);
 }
 
 hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
@@ -1206,8 +1269,11 @@ hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts
     return hipGetLastError();
 }
 
-hipError_t launch_zero_fill(double *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_c, dim3(nblk(m, 256), ydim(n)), dim3(256), 0, s, C, m, n, ldc);
+hipError_t launch_zero_fill(Elem el, void *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s) {
+    if (el == Elem::f32)
+        hipLaunchKernelGGL(k_zero_c<float>, dim3(nblk(m, 256), ydim(n)), dim3(256), 0, s, (float *)C, m, n, ldc);
+    else
+        hipLaunchKernelGGL(k_zero_c<double>, dim3(nblk(m, 256), ydim(n)), dim3(256), 0, s, (double *)C, m, n, ldc);
     return hipGetLastError();
 }
 

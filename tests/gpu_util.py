@@ -23,10 +23,12 @@ INT32_MIN = -(2 ** 31)
 
 
 def device_colmajor(X: np.ndarray, ld: int | None = None) -> torch.Tensor:
-    """Column-major copy of X (rows x cols) on the GPU with leading dimension ld."""
+    """Column-major copy of X (rows x cols) on the GPU with leading dimension ld
+    (float32 for a float32 X, else float64)."""
     rows, cols = X.shape
     ld = max(rows, 1) if ld is None else ld
-    t = torch.zeros((max(cols, 1), ld), dtype=torch.float64)
+    dt = torch.float32 if X.dtype == np.float32 else torch.float64
+    t = torch.zeros((max(cols, 1), ld), dtype=dt)
     if rows and cols:
         t[:cols, :rows] = torch.from_numpy(np.ascontiguousarray(X.T))
     return t.cuda()
@@ -37,7 +39,9 @@ def stream_handle() -> int:
 
 
 def run_debug(A, B, N, mode="fast", lda=None, ldb=None, ldc=None, want_prod=True, want_res=True):
-    """One ozaki2_dgemm_debug call; returns numpy copies of C and intermediates."""
+    """One ozaki2_dgemm_debug call (ozaki2_sgemm_debug for float32 operands);
+    returns numpy copies of C and intermediates."""
+    single = A.dtype == np.float32
     m, k = A.shape
     n = B.shape[1]
     md = oz.MODES[mode]
@@ -46,7 +50,8 @@ def run_debug(A, B, N, mode="fast", lda=None, ldb=None, ldc=None, want_prod=True
     ldc = max(m, 1) if ldc is None else ldc
     dA = device_colmajor(A, lda)
     dB = device_colmajor(B, ldb)
-    dC = torch.full((max(n, 1), ldc), float("nan"), dtype=torch.float64, device="cuda")
+    dC = torch.full((max(n, 1), ldc), float("nan"), dtype=torch.float32 if single else torch.float64,
+                    device="cuda")
     wbytes = oz.ozaki2_debug_workspace_size(m, n, k, N, md)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device="cuda")
     e = torch.empty(max(m, 1), dtype=torch.int32, device="cuda")
@@ -55,13 +60,14 @@ def run_debug(A, B, N, mode="fast", lda=None, ldb=None, ldc=None, want_prod=True
     rb = torch.empty((N, n, k) if want_res else (1,), dtype=torch.int8, device="cuda")
     prod = torch.empty((N, n, m) if want_prod else (1,), dtype=torch.int32, device="cuda")
     red = torch.empty((N, n, m), dtype=torch.uint8, device="cuda")
-    st = oz.ozaki2_dgemm_debug(m, n, k, dA.data_ptr(), lda, dB.data_ptr(), ldb, dC.data_ptr(), ldc, N, md,
-                               ws.data_ptr(), wbytes, e.data_ptr(), f.data_ptr(),
-                               ra.data_ptr() if want_res else None, rb.data_ptr() if want_res else None,
-                               prod.data_ptr() if want_prod else None, red.data_ptr(), stream_handle())
+    debug = oz.ozaki2_sgemm_debug if single else oz.ozaki2_dgemm_debug
+    st = debug(m, n, k, dA.data_ptr(), lda, dB.data_ptr(), ldb, dC.data_ptr(), ldc, N, md,
+               ws.data_ptr(), wbytes, e.data_ptr(), f.data_ptr(),
+               ra.data_ptr() if want_res else None, rb.data_ptr() if want_res else None,
+               prod.data_ptr() if want_prod else None, red.data_ptr(), stream_handle())
     assert st == 0, oz.status_string(st)
     torch.cuda.synchronize()
-    out = dict(C=dC[:n, :m].cpu().numpy().T.copy() if n and m else np.zeros((m, n)),
+    out = dict(C=dC[:n, :m].cpu().numpy().T.copy() if n and m else np.zeros((m, n), dtype=A.dtype),
                e=e[:m].cpu().numpy(), f=f[:n].cpu().numpy(), red=red.cpu().numpy())
     if want_res:
         out["RA"] = ra.cpu().numpy()
@@ -73,17 +79,19 @@ def run_debug(A, B, N, mode="fast", lda=None, ldb=None, ldc=None, want_prod=True
 
 
 def run_ws(A, B, N, mode="fast"):
-    """ozaki2_dgemm_ws on freshly uploaded operands; returns C (numpy)."""
+    """ozaki2_dgemm_ws (ozaki2_sgemm_ws for float32) on freshly uploaded operands; returns C (numpy)."""
+    single = A.dtype == np.float32
     m, k = A.shape
     n = B.shape[1]
     md = oz.MODES[mode]
     dA = device_colmajor(A)
     dB = device_colmajor(B)
-    dC = torch.empty((max(n, 1), max(m, 1)), dtype=torch.float64, device="cuda")
+    dC = torch.empty((max(n, 1), max(m, 1)), dtype=torch.float32 if single else torch.float64, device="cuda")
     wbytes = oz.ozaki2_workspace_size(m, n, k, N, md)
     ws = torch.empty(max(wbytes, 1), dtype=torch.uint8, device="cuda")
-    st = oz.ozaki2_dgemm_ws(m, n, k, dA.data_ptr(), max(m, 1), dB.data_ptr(), max(k, 1), dC.data_ptr(), max(m, 1),
-                            N, md, ws.data_ptr(), wbytes, stream_handle())
+    fn = oz.ozaki2_sgemm_ws if single else oz.ozaki2_dgemm_ws
+    st = fn(m, n, k, dA.data_ptr(), max(m, 1), dB.data_ptr(), max(k, 1), dC.data_ptr(), max(m, 1),
+            N, md, ws.data_ptr(), wbytes, stream_handle())
     assert st == 0, oz.status_string(st)
     torch.cuda.synchronize()
     return dC[:n, :m].cpu().numpy().T.copy()
@@ -123,8 +131,10 @@ def assert_bitwise_equal(a: np.ndarray, b: np.ndarray, what: str):
     assert a.shape == b.shape, (what, a.shape, b.shape)
     na, nb = np.isnan(a), np.isnan(b)
     assert np.array_equal(na, nb), f"{what}: NaN positions differ"
-    av = np.where(na, 0.0, a).view(np.uint64)
-    bv = np.where(nb, 0.0, b).view(np.uint64)
+    assert a.dtype == b.dtype, (what, a.dtype, b.dtype)
+    bits = np.uint32 if a.dtype == np.float32 else np.uint64
+    av = np.where(na, a.dtype.type(0), a).view(bits)
+    bv = np.where(nb, b.dtype.type(0), b).view(bits)
     if not np.array_equal(av, bv):
         idx = np.argwhere(av != bv)
         i = tuple(idx[0])
@@ -132,13 +142,15 @@ def assert_bitwise_equal(a: np.ndarray, b: np.ndarray, what: str):
 
 
 def full_parity(A, B, N, mode="fast", **kw):
-    """Debug run on the GPU vs the oracle at every stage; returns (gpu, oracle, mismatches)."""
+    """Debug run on the GPU vs the oracle at every stage; returns (gpu, oracle, mismatches).
+    float32 operands go through ozaki2_sgemm_debug and the oracle's os2_sgemm."""
+    emul = O.os2_sgemm if A.dtype == np.float32 else O.os2_dgemm
     g = run_debug(A, B, N, mode, **kw)
-    r = O.os2_dgemm(A, B, N, mode)
-    e, ne = reconcile_exponents(g["e"], r["e"], A, N, mode)
-    f, nf = reconcile_exponents(g["f"], r["f"], np.asarray(B).T, N, mode)
+    r = emul(A, B, N, mode)
+    e, ne = reconcile_exponents(g["e"], r["e"], A.astype(np.float64), N, mode)
+    f, nf = reconcile_exponents(g["f"], r["f"], np.asarray(B, dtype=np.float64).T, N, mode)
     if ne or nf:
-        r = O.os2_dgemm(A, B, N, mode, e=e, f=f)
+        r = emul(A, B, N, mode, e=e, f=f)
     okr = np.array([v is not None for v in r["e"]])
     okc = np.array([v is not None for v in r["f"]])
     assert np.array_equal(g["RA"][:, okr, :], r["RA"][:, okr, :]), "int8 residues of A differ"

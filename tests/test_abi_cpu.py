@@ -86,6 +86,8 @@ P = 1 << 20  # a fake non-null pointer: validation fails before it is ever used
 def test_status_codes(args, status):
     assert oz.ozaki2_dgemm(*args, 0) == status
     assert oz.ozaki2_dgemm_ws(*args, P, 1 << 40, 0) == status
+    assert oz.ozaki2_sgemm(*args, 0) == status
+    assert oz.ozaki2_sgemm_ws(*args, P, 1 << 40, 0) == status
 
 
 def test_workspace_checks():

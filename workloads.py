@@ -19,7 +19,8 @@ No public dataset is involved: the pages' workloads are themselves synthetic.
 Conventions
 -----------
 Every generator returns numpy float64 arrays ``A`` of shape (m, k) and ``B`` of
-shape (k, n) in natural mathematical orientation. Random numbers are drawn
+shape (k, n) in natural mathematical orientation (``make`` rounds them to
+binary32 for the single-precision workload). Random numbers are drawn
 with ``numpy.random.default_rng(seed)`` (PCG64), A's arrays first and then B's,
 each in C order. Callers convert to column-major storage themselves.
 """
@@ -78,14 +79,24 @@ CONFIGS = {
     "scale_sweep_2048_n14": dict(m=2048, n=2048, k=2048, num_moduli=14, kind="sweep", seed=0),
     # 16384^3, phi=1.0, N=18 (2 GiB per operand).
     "spread1.0_16384_n18": dict(m=16384, n=16384, k=16384, num_moduli=18, kind="spread", phi=1.0, seed=0),
+    # Single precision ("Improved Scaling ...", section Zentrale Beiträge: the
+    # scheme is also evaluated for SGEMM): the phi=1.0 draw at 4096^3 rounded
+    # to binary32, N=8.
+    "sgemm_spread1.0_4096_n8": dict(m=4096, n=4096, k=4096, num_moduli=8, kind="spread", phi=1.0, seed=0,
+                                    single=True),
 }
 
 
 def make(name: str):
-    """Operands (A, B) of a named workload (not for the scale sweep)."""
+    """Operands (A, B) of a named workload (not for the scale sweep); binary32
+    arrays (the float64 draw rounded to nearest) for single-precision ones."""
     c = CONFIGS[name]
     if c["kind"] == "uniform":
-        return uniform_case(c["m"], c["n"], c["k"], c["seed"])
-    if c["kind"] == "spread":
-        return spread_case(c["m"], c["n"], c["k"], c["phi"], c["seed"])
-    raise ValueError(f"{name} is a sweep; use scale_sweep_case()")
+        a, b = uniform_case(c["m"], c["n"], c["k"], c["seed"])
+    elif c["kind"] == "spread":
+        a, b = spread_case(c["m"], c["n"], c["k"], c["phi"], c["seed"])
+    else:
+        raise ValueError(f"{name} is a sweep; use scale_sweep_case()")
+    if c.get("single"):
+        return a.astype(np.float32), b.astype(np.float32)
+    return a, b
