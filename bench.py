@@ -87,22 +87,27 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
     n = B.shape[1]
     rows = rows_wanted or max(8, min(m, int(3072 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
     rows = min(rows, m)
+    single = A.dtype == np.float32
+    emul = O.os2_sgemm if single else O.os2_dgemm
     log(f"cpu_baseline: oracle on {rows} rows x {n} columns, k={k}, N={N}, {mode}")
     t0 = time.perf_counter()
-    r = O.os2_dgemm(A[:rows], B, N, mode)
+    r = emul(A[:rows], B, N, mode)
     t = time.perf_counter() - t0
     value = 2.0 * rows * n * k / t / 1e12
     Cs = C_gpu[:rows]
-    diff = (Cs.view(np.uint64) != r["C"].view(np.uint64)) & ~(np.isnan(Cs) & np.isnan(r["C"]))
+    bits = np.uint32 if single else np.uint64
+    diff = (Cs.view(bits) != r["C"].view(bits)) & ~(np.isnan(Cs) & np.isnan(r["C"]))
     er = min(rows, 128)  # accuracy against the double-double reference on the first rows
-    hi, lo = O.dd_gemm(A[:er], B)
-    err = O.error_metrics(Cs[:er], hi, lo, A[:er], B)
-    native = O.error_metrics(A[:er] @ B, hi, lo, A[:er], B)
+    A64, B64 = A[:er].astype(np.float64), B.astype(np.float64)
+    hi, lo = O.dd_gemm(A64, B64)
+    err = O.error_metrics(Cs[:er].astype(np.float64), hi, lo, A64, B64)
+    native = O.error_metrics((A[:er] @ B).astype(np.float64), hi, lo, A64, B64)
+    nat = "fp32" if single else "fp64"
     return dict(value=value, unit="TFLOPS", cores=max(omp_threads, blas_threads), kind="oracle",
                 sample=f"rows 0..{rows - 1} of A times all of B ({rows}x{n}x{k}, N={N}, {mode}); "
                        f"{t:.2f} s; OpenMP {omp_threads} threads, BLAS {blas_threads} threads"), \
         dict(parity_mismatches=int(diff.sum()), parity_entries=int(Cs.size), error_rows=er, **err,
-             native_fp64_E_cw=native["E_cw"], native_fp64_E_el=native["E_el"])
+             **{f"native_{nat}_E_cw": native["E_cw"], f"native_{nat}_E_el": native["E_el"]})
 
 
 def main():
@@ -134,13 +139,15 @@ def main():
     if cfg["kind"] == "sweep":
         raise SystemExit("the scale sweep is a parity-test case, not a bench line")
     m, n, k, N = cfg["m"], cfg["n"], cfg["k"], cfg["num_moduli"]
+    single = bool(cfg.get("single"))
     md = oz.MODES[args.mode]
     log(f"generating {args.config} ({m}x{k} @ {k}x{n}), N={N}, mode={args.mode}")
     A, B = W.make(args.config)
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)  # column-major A, lda = m
     dB = torch.from_numpy(np.ascontiguousarray(B.T)).to(dev)  # column-major B, ldb = k
-    dC = torch.empty((n, m), dtype=torch.float64, device=dev)
+    dC = torch.empty((n, m), dtype=torch.float32 if single else torch.float64, device=dev)
+    gemm_ws = oz.ozaki2_sgemm_ws if single else oz.ozaki2_dgemm_ws
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def workspace(mode_id):
@@ -152,8 +159,8 @@ def main():
     def step(mode_id=md, w=None, wb=None):
         w = ws if w is None else w
         wb = wbytes if wb is None else wb
-        st = oz.ozaki2_dgemm_ws(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, mode_id,
-                                w.data_ptr(), wb, stream)
+        st = gemm_ws(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, mode_id, w.data_ptr(), wb,
+                     stream)
         if st:
             raise RuntimeError(oz.status_string(st))
 
@@ -205,8 +212,34 @@ def main():
         At = torch.from_numpy(A).to(dev)
         Bt = torch.from_numpy(B).to(dev)
         ms3 = time_steps(lambda: torch.mm(At, Bt), max(args.steps // 2, 3), 2, torch)
-        extras["native_fp64_gemm_tflops"] = round(flops / (ms3 * 1e-3) / 1e12, 3)
+        extras[f"native_fp{32 if single else 64}_gemm_tflops"] = round(flops / (ms3 * 1e-3) / 1e12, 3)
         del At, Bt
+        if not single:
+            # the single-precision emulation ([G] Zentrale Beiträge) on its 4096^3 workload, as context
+            As, Bs = W.make("sgemm_spread1.0_4096_n8")
+            cs = W.CONFIGS["sgemm_spread1.0_4096_n8"]
+            ms_, ns_, ks_, Ns = cs["m"], cs["n"], cs["k"], cs["num_moduli"]
+            dAs = torch.from_numpy(np.ascontiguousarray(As.T)).to(dev)
+            dBs = torch.from_numpy(np.ascontiguousarray(Bs.T)).to(dev)
+            dCs = torch.empty((ns_, ms_), dtype=torch.float32, device=dev)
+            wbs = oz.ozaki2_workspace_size(ms_, ns_, ks_, Ns, oz.FAST)
+            wss = torch.empty(wbs, dtype=torch.uint8, device=dev)
+
+            def sstep():
+                st = oz.ozaki2_sgemm_ws(ms_, ns_, ks_, dAs.data_ptr(), ms_, dBs.data_ptr(), ks_, dCs.data_ptr(), ms_,
+                                        Ns, oz.FAST, wss.data_ptr(), wbs, stream)
+                if st:
+                    raise RuntimeError(oz.status_string(st))
+
+            ms5 = time_steps(sstep, max(args.steps, 5), 3, torch)
+            sflops = 2.0 * ms_ * ns_ * ks_
+            extras["sgemm_n8_tflops"] = round(sflops / (ms5 * 1e-3) / 1e12, 3)
+            extras["sgemm_n8_ms_per_step"] = round(ms5, 4)
+            Ats = torch.from_numpy(As).to(dev)
+            Bts = torch.from_numpy(Bs).to(dev)
+            ms6 = time_steps(lambda: torch.mm(Ats, Bts), max(args.steps // 2, 3), 2, torch)
+            extras["native_fp32_gemm_tflops"] = round(sflops / (ms6 * 1e-3) / 1e12, 3)
+            del dAs, dBs, dCs, wss, Ats, Bts
         # the vendor INT8 GEMM (torch._int_mm = hipBLASLt) on random int8 of one
         # modulus' shape, as context for the INT8 roofline fraction
         try:
@@ -224,7 +257,8 @@ def main():
         cpu, accuracy = cpu_baseline_leg(A, B, C, N, args.mode, args.cpu_rows)
 
     line = dict(
-        metric="emulated FP64 TFLOPS (2mnk/t) at 4096^3, % INT8 MFMA peak; max rel err",
+        metric=("emulated FP32 TFLOPS (2mnk/t)" if single else
+                "emulated FP64 TFLOPS (2mnk/t) at 4096^3, % INT8 MFMA peak; max rel err"),
         value=round(tflops, 3), unit="TFLOPS", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="int8", data="synthetic",
