@@ -45,6 +45,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * Single precision ([G] section Zentrale Beiträge names SGEMM): the same
     steps on the binary32 inputs widened exactly to doubles, and one rounding
     of X * 2^-(e+f) to binary32 (os2_sgemm, round_to_f32).
+  * Complex products ([G] closing remark, future work there): one exponent
+    per row/column from the complex 2-norm, parts truncated separately, and
+    Gauss' three products per modulus, which are exact in residues
+    (os2_zgemm; fast mode only).
   * Accurate mode ([Q] section 2の累乗による整数化, [G] section
     Problemstellung) is read as: bound |A| and |B| from above by 6-bit
     integers on the row/column maxima, form their product with one extra
@@ -535,6 +539,88 @@ def os2_sgemm(A, B, num_moduli: int, mode: str = "fast", e=None, f=None) -> dict
     r["C64"] = r["C"]
     r["C"] = unscale_f32(r["X"], r["e"], r["f"])
     return r
+
+
+# --------------------------------------------------------------------------
+# Complex products ([G] closing remark: the approach also applies to complex
+# products, ZGEMM/CGEMM, left there as future work)
+# --------------------------------------------------------------------------
+# Reading (each item is listed in the design doc):
+#  * A = Ar + i Ai, B = Br + i Bi. Row i of A takes one exponent, from its
+#    complex 2-norm sum_h (ar^2 + ai^2), with the formula of [G] Methodik;
+#    column j of B likewise. By Cauchy-Schwarz, 2 mu ||a_i|| ||b_j|| nu <= P - 1
+#    bounds both the real and the imaginary part of the exact integer product
+#    by (P - 1) / 2.
+#  * The two parts are truncated separately: ar' = trunc(2^e ar), ai' likewise.
+#  * Xr = sum_h ar'br' - ai'bi' and Xi = sum_h ar'bi' + ai'br' exactly, and
+#    C = RN(Xr) 2^-(e+f) + i RN(Xi) 2^-(e+f) (binary32 parts: one rounding
+#    each, as round_to_f32).
+#  * In residues the three products of Gauss' trick are exact: per modulus
+#    T1 = ar'br', T2 = ai'bi', T3 = (ar' + ai')(br' + bi'), and
+#    Xr = T1 - T2, Xi = T3 - T1 - T2 (mod p), so three integer GEMMs per
+#    modulus give both parts with no rounding at all.
+#  * Only the fast mode is defined for complex operands.
+def sym_mod(x: np.ndarray, p: int) -> np.ndarray:
+    """x mod p in the symmetric range of [Q] step 2, as int8 (for p = 256 the
+    class of 128 is stored as -128)."""
+    h = (p - 1) // 2 if p % 2 else p // 2
+    return (np.mod(np.asarray(x, dtype=np.int64) + h, p) - h).astype(np.int8)
+
+
+def complex_exponents_rows(Xr: np.ndarray, Xi: np.ndarray, Pp: float) -> list:
+    """Fast-mode exponent of each row of a complex matrix from sum_h (re^2 + im^2)."""
+    return fast_exponents_rows(np.concatenate([np.asarray(Xr, np.float64), np.asarray(Xi, np.float64)], axis=1), Pp)
+
+
+def os2_zgemm(A, B, num_moduli: int, e=None, f=None, single: bool = False) -> dict:
+    """The emulation of a complex product C = A B (A (m, k), B (k, n) complex),
+    with every intermediate: residue planes of the real parts, imaginary parts
+    and their sums, the three products per modulus and their residues, the
+    residues of both parts, the exact parts Xr, Xi and C. single: binary32
+    parts (inputs widened exactly, each part rounded once to binary32)."""
+    cdt = np.complex64 if single else np.complex128
+    A = np.asarray(A, dtype=cdt).astype(np.complex128)
+    B = np.asarray(B, dtype=cdt).astype(np.complex128)
+    moduli = choose_moduli(num_moduli)
+    tables = crt_tables(moduli)
+    Pp = scaling_constant(tables["P"])
+    if e is None:
+        e = complex_exponents_rows(A.real, A.imag, Pp)
+    if f is None:
+        f = complex_exponents_rows(B.real.T, B.imag.T, Pp)
+    okr = np.array([v is not None for v in e], dtype=bool)
+    okc = np.array([v is not None for v in f], dtype=bool)
+    A0 = np.where(okr[:, None], A, 0.0)
+    B0 = np.where(okc[None, :], B, 0.0)
+    RAr, RAi = split(A0.real, e, moduli), split(A0.imag, e, moduli)
+    RBr, RBi = split(B0.real.T, f, moduli), split(B0.imag.T, f, moduli)
+    RAs = np.stack([sym_mod(RAr[l].astype(np.int64) + RAi[l], p) for l, p in enumerate(moduli)])
+    RBs = np.stack([sym_mod(RBr[l].astype(np.int64) + RBi[l], p) for l, p in enumerate(moduli)])
+    T1 = residue_products(RAr, RBr)
+    T2 = residue_products(RAi, RBi)
+    T3 = residue_products(RAs, RBs)
+    T = np.stack([T1, T2, T3], axis=1)  # [N][3][m][n]
+    cT = np.stack([reduce_products(T[:, g], moduli) for g in range(3)], axis=1)
+    cr = reduce_products(T1 - T2, moduli)
+    ci = reduce_products(T3 - T1 - T2, moduli)
+    Xr = crt(cr, tables)
+    Xi = crt(ci, tables)
+    Cr, Ci = (unscale_f32(Xr, e, f), unscale_f32(Xi, e, f)) if single else (unscale(Xr, e, f), unscale(Xi, e, f))
+    C = np.empty(Cr.shape, dtype=np.complex64 if single else np.complex128)
+    C.real[...] = Cr
+    C.imag[...] = Ci
+    return dict(moduli=moduli, tables=tables, e=e, f=f, RAr=RAr, RAi=RAi, RAs=RAs, RBr=RBr, RBi=RBi,
+                RBs=RBs, T=T, cT=cT, cr=cr, ci=ci, Xr=Xr, Xi=Xi, C=C)
+
+
+def exact_complex_scaled_product(A, B, e, f):
+    """(Xr, Xi) from the plain definition: exact sums of products of the
+    truncated scaled parts, with Python integers (small cases only)."""
+    A = np.asarray(A, dtype=np.complex128)
+    B = np.asarray(B, dtype=np.complex128)
+    ar, ai = scaled_integers(A.real, e), scaled_integers(A.imag, e)
+    br, bi = scaled_integers(B.real.T, f), scaled_integers(B.imag.T, f)
+    return ar.dot(br.T) - ai.dot(bi.T), ar.dot(bi.T) + ai.dot(br.T)
 
 
 def exact_scaled_product(A, B, e, f) -> np.ndarray:

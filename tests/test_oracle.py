@@ -447,3 +447,99 @@ def test_sgemm_accuracy_against_native_fp32():
         assert ecw(O.os2_sgemm(A, B, N)["C"]) <= ecw(A @ B), (phi, N)
         # and never worse than the final binary32 rounding allows
         assert ecw(O.os2_sgemm(A, B, 10)["C"]) <= 2.0 ** -24
+
+
+# --------------------------------------------------------------------------
+# Complex products: Gauss' three products per modulus, exact in residues
+# --------------------------------------------------------------------------
+def _complex_case(m, n, k, seed, phi=1.0):
+    rng = np.random.default_rng(seed)
+    parts = [W.spread_matrix(rng, shape, phi) for shape in ((m, k), (m, k), (k, n), (k, n))]
+    return parts[0] + 1j * parts[1], parts[2] + 1j * parts[3]
+
+
+def test_sym_mod_ranges():
+    for p in (3, 173, 255, 256):
+        x = np.arange(-3 * p, 3 * p)
+        r = O.sym_mod(x, p).astype(np.int64)
+        assert np.all((r - x) % p == 0)
+        lo, hi = (-(p - 1) // 2, (p - 1) // 2) if p % 2 else (-p // 2, p // 2 - 1)
+        assert r.min() == lo and r.max() == hi
+
+
+@pytest.mark.parametrize("N", [4, 8, 16, 18])
+def test_complex_rns_equals_plain_definition(N):
+    A, B = _complex_case(11, 9, 23, seed=N)
+    A[2] = 0.0
+    A[5, 3] = complex(np.inf, 0.0)
+    B[4, 6] = complex(0.0, np.nan)
+    r = O.os2_zgemm(A, B, N)
+    assert r["e"][5] is None and r["f"][6] is None and r["e"][2] == 0
+    okr = [v is not None for v in r["e"]]
+    okc = [v is not None for v in r["f"]]
+    A0 = np.where(np.array(okr)[:, None], A, 0.0)
+    B0 = np.where(np.array(okc)[None, :], B, 0.0)
+    e0 = [v if v is not None else 0 for v in r["e"]]
+    f0 = [v if v is not None else 0 for v in r["f"]]
+    Xr, Xi = O.exact_complex_scaled_product(A0, B0, e0, f0)
+    for i in range(11):
+        for j in range(9):
+            if okr[i] and okc[j]:
+                assert int(r["Xr"][i, j]) == Xr[i, j] and int(r["Xi"][i, j]) == Xi[i, j]
+                s = -(e0[i] + f0[j])
+                assert r["C"][i, j].real == math.ldexp(float(Xr[i, j]), s)
+                assert r["C"][i, j].imag == math.ldexp(float(Xi[i, j]), s)
+            else:
+                assert np.isnan(r["C"][i, j].real) and np.isnan(r["C"][i, j].imag)
+    # the residues of both parts are the CRT images of the exact parts
+    for l, p in enumerate(r["moduli"]):
+        for i in range(11):
+            for j in range(9):
+                if okr[i] and okc[j]:
+                    assert r["cr"][l, i, j] == Xr[i, j] % p and r["ci"][l, i, j] == Xi[i, j] % p
+
+
+def test_complex_gaussian_integers_give_the_exact_product():
+    rng = np.random.default_rng(3)
+    A = rng.integers(-3, 4, (14, 40)) + 1j * rng.integers(-3, 4, (14, 40))
+    B = rng.integers(-3, 4, (40, 10)) + 1j * rng.integers(-3, 4, (40, 10))
+    assert np.array_equal(O.os2_zgemm(A, B, 8)["C"], A @ B)
+    assert np.array_equal(O.os2_zgemm(A, B, 8, single=True)["C"], (A @ B).astype(np.complex64))
+
+
+def test_complex_exponents_keep_both_parts_in_range():
+    # 2 ||a_i'|| ||b_j'|| <= P - 1 on the truncated integers (complex 2-norms),
+    # which bounds |Re| and |Im| of every product entry by (P - 1) / 2
+    A, B = _complex_case(20, 16, 64, seed=5, phi=2.0)
+    for N in (6, 14, 16):
+        r = O.os2_zgemm(A, B, N)
+        P = r["tables"]["P"]
+        ar, ai = O.scaled_integers(A.real, r["e"]), O.scaled_integers(A.imag, r["e"])
+        br, bi = O.scaled_integers(B.real.T, r["f"]), O.scaled_integers(B.imag.T, r["f"])
+        na = [sum(int(x) ** 2 for x in ar[i]) + sum(int(x) ** 2 for x in ai[i]) for i in range(20)]
+        nb = [sum(int(x) ** 2 for x in br[j]) + sum(int(x) ** 2 for x in bi[j]) for j in range(16)]
+        for i in range(20):
+            for j in range(16):
+                assert 4 * na[i] * nb[j] <= (P - 1) ** 2
+                assert 2 * abs(int(r["Xr"][i, j])) <= P - 1 and 2 * abs(int(r["Xi"][i, j])) <= P - 1
+
+
+def test_complex_scale_law():
+    A, B = _complex_case(9, 7, 30, seed=8)
+    base = O.os2_zgemm(A, B, 14)["C"]
+    for s in (-40, 40):
+        got = O.os2_zgemm(np.ldexp(A.real, s) + 1j * np.ldexp(A.imag, s), B, 14)["C"]
+        assert np.array_equal(got, np.ldexp(base.real, s) + 1j * np.ldexp(base.imag, s))
+
+
+def test_complex_accuracy_against_native():
+    A, B = _complex_case(48, 40, 300, seed=9)
+    rr = [O.dd_gemm(X, Y) for X, Y in ((A.real, B.real), (A.imag, B.imag), (A.real, B.imag), (A.imag, B.real))]
+    ref_r = (rr[0][0] - rr[1][0]) + (rr[0][1] - rr[1][1])
+    ref_i = (rr[2][0] + rr[3][0]) + (rr[2][1] + rr[3][1])
+    scale = np.abs(A) @ np.abs(B)
+    ecw = lambda C: float(np.max(np.maximum(np.abs(C.real - ref_r), np.abs(C.imag - ref_i)) / scale))
+    assert ecw(O.os2_zgemm(A, B, 16)["C"]) <= ecw(A @ B)
+    assert ecw(O.os2_zgemm(A, B, 16)["C"]) <= 1e-15
+    assert ecw(O.os2_zgemm(A, B, 8, single=True)["C"].astype(np.complex128)) <= \
+        ecw((A.astype(np.complex64) @ B.astype(np.complex64)).astype(np.complex128))
