@@ -191,6 +191,58 @@ int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
                        int32_t *prod_out, uint8_t *red_out, void *stream);
 
+/*
+ * Complex products: C := A * B for double complex (ozaki2_zgemm*) or float
+ * complex (ozaki2_cgemm*) matrices, the extension to complex products that
+ * [G] names in its closing remark (ZGEMM/CGEMM, future work there).
+ * A, B, C hold interleaved (re, im) pairs, column-major, and lda, ldb, ldc
+ * count complex elements (element (i, h) of A at A[2*(i + h*lda)] and the next
+ * value); other arguments, checks and status codes as ozaki2_dgemm.
+ * Row i of A (column j of B) gets one fast-mode exponent from its complex
+ * 2-norm sum_h (re^2 + im^2); the parts are truncated separately, and per
+ * modulus three INT8 products give T1 = re*re, T2 = im*im and
+ * T3 = (re+im)*(re+im), so that Re = T1 - T2 and Im = T3 - T1 - T2 hold
+ * exactly in residues (Gauss' three-multiplication form, with no rounding).
+ * Each part of C is then the exact integer rounded once, as for real products
+ * (binary32 parts for cgemm). Only OZAKI2_FAST is supported: mode
+ * OZAKI2_ACCURATE returns OZAKI2_ERR_UNSUPPORTED.
+ * Debug copies (zgemm/cgemm _debug) use 3N planes in place of N, plane 3l + g
+ * for modulus l and product g (g = 0: re*re, 1: im*im, 2: sums), e.g.
+ * resA_out int8 [3N][m][k], red_out uint8 [3N][n][m].
+ */
+int ozaki2_zgemm(int64_t m, int64_t n, int64_t k,
+                 const double *A, int64_t lda, const double *B, int64_t ldb,
+                 double *C, int64_t ldc, int num_moduli, int mode, void *stream);
+int ozaki2_zgemm_ws(int64_t m, int64_t n, int64_t k,
+                    const double *A, int64_t lda, const double *B, int64_t ldb,
+                    double *C, int64_t ldc, int num_moduli, int mode,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int ozaki2_zgemm_debug(int64_t m, int64_t n, int64_t k,
+                       const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode,
+                       void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
+                       int32_t *prod_out, uint8_t *red_out, void *stream);
+int ozaki2_cgemm(int64_t m, int64_t n, int64_t k,
+                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int num_moduli, int mode, void *stream);
+int ozaki2_cgemm_ws(int64_t m, int64_t n, int64_t k,
+                    const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float *C, int64_t ldc, int num_moduli, int mode,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int ozaki2_cgemm_debug(int64_t m, int64_t n, int64_t k,
+                       const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc, int num_moduli, int mode,
+                       void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out,
+                       int32_t *prod_out, uint8_t *red_out, void *stream);
+
+/*
+ * Bytes of device workspace the complex _ws entry points need (debug != 0:
+ * the _debug ones); 0 for invalid arguments or empty products. Host-only.
+ */
+size_t ozaki2_zgemm_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int debug);
+
 /* Workspace bytes for ozaki2_dgemm_debug (larger: raw int32 products). */
 size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
 

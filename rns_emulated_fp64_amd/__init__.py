@@ -28,6 +28,8 @@ EXPORTS = (
     "ozaki2_debug_workspace_size", "ozaki2_max_moduli", "ozaki2_moduli", "ozaki2_scaling_constant",
     "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
     "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
+    "ozaki2_zgemm", "ozaki2_zgemm_ws", "ozaki2_zgemm_debug", "ozaki2_cgemm", "ozaki2_cgemm_ws", "ozaki2_cgemm_debug",
+    "ozaki2_zgemm_workspace_size",
 )
 
 _lib = None
@@ -59,10 +61,12 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_dgemm_ws.restype = i32
     L.ozaki2_dgemm_debug.argtypes = prod + [p, sz, p, p, p, p, p, p, p]
     L.ozaki2_dgemm_debug.restype = i32
-    for name in ("ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug"):
-        twin = getattr(L, name.replace("sgemm", "dgemm"))
-        getattr(L, name).argtypes = twin.argtypes
-        getattr(L, name).restype = i32
+    for prefix in ("ozaki2_sgemm", "ozaki2_zgemm", "ozaki2_cgemm"):
+        for suffix in ("", "_ws", "_debug"):
+            getattr(L, prefix + suffix).argtypes = getattr(L, "ozaki2_dgemm" + suffix).argtypes
+            getattr(L, prefix + suffix).restype = i32
+    L.ozaki2_zgemm_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.ozaki2_zgemm_workspace_size.restype = sz
     L.ozaki2_crt_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, sz, p]
     L.ozaki2_crt_debug.restype = i32
     L.ozaki2_max_moduli.argtypes = []
@@ -122,6 +126,40 @@ def ozaki2_sgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, worksp
                        e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
     return lib().ozaki2_sgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
                                     e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_zgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode=FAST, stream=0) -> int:
+    return lib().ozaki2_zgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_zgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_zgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                 stream)
+
+
+def ozaki2_zgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                       e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
+    return lib().ozaki2_zgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                    e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_cgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode=FAST, stream=0) -> int:
+    return lib().ozaki2_cgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_cgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_cgemm_ws(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                 stream)
+
+
+def ozaki2_cgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                       e_out, f_out, resA_out, resB_out, prod_out, red_out, stream=0) -> int:
+    return lib().ozaki2_cgemm_debug(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                    e_out, f_out, resA_out, resB_out, prod_out, red_out, stream)
+
+
+def ozaki2_zgemm_workspace_size(m, n, k, num_moduli, debug=False) -> int:
+    return lib().ozaki2_zgemm_workspace_size(m, n, k, num_moduli, 1 if debug else 0)
 
 
 def ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream=0) -> int:

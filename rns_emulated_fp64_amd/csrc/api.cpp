@@ -48,7 +48,9 @@ bool layout_fits(int64_t m, int64_t n, int64_t k, int mode) {
     return m < lim && n < lim && k <= (mode == OZAKI2_ACCURATE ? OZAKI2_MAX_K_ACCURATE : OZAKI2_MAX_K);
 }
 
-Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool debug) {
+// group: residue planes per modulus, 1 for real products, 3 for complex ones
+// (real parts, imaginary parts, their sums).
+Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool debug, int group = 1) {
     Layout L{};
     L.m_pad = round_up(m > 0 ? m : 1, kTileM);
     L.n_pad = round_up(n > 0 ? n : 1, kTileN);
@@ -85,10 +87,11 @@ Layout make_layout(int64_t m, int64_t n, int64_t k, int nmod, int mode, bool deb
         L.abar = take(mp * kp);
         L.bbar = take(np * kp);
     }
-    L.ra = take((size_t)nmod * mp * kp);
-    L.rb = take((size_t)nmod * np * kp);
-    L.planes = take((size_t)nmod * np * mp);
-    if (debug) L.raw = take(4 * (size_t)nmod * np * mp);
+    const size_t planes = (size_t)nmod * group;
+    L.ra = take(planes * mp * kp);
+    L.rb = take(planes * np * kp);
+    L.planes = take(planes * np * mp);
+    if (debug) L.raw = take(4 * planes * np * mp);
     L.total = off;
     return L;
 }
@@ -147,8 +150,8 @@ struct DebugOut {
     uint8_t *red;
 };
 
-int run(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb, void *C,
-        int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
+int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
+        void *C, int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
     const Tables *T = get_tables(nmod);
     // Timing events (start/stop per phase) are recorded before the first and
     // after the last kernel of a phase; unless all phases were asked for, only
@@ -177,7 +180,8 @@ int run(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, co
 
     // Step 1: squared norms of the rows of A and exponents of the columns of
     // B ([G] Methodik), one launch.
-    HIP_TRY(launch_scale(el, A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
+    const int group = cplx ? 3 : 1;
+    HIP_TRY(launch_scale(el, cplx, A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
     if (accurate) {
         // Accurate mode bounds the products with one extra INT8 GEMM first
         // ([G] Problemstellung).
@@ -195,55 +199,62 @@ int run(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, co
 
     // Steps 1 + 2: integerize and split both operands into residues, one
     // launch (in fast mode it also finishes the row exponents of A).
-    HIP_TRY(launch_split(el, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
+    HIP_TRY(launch_split(el, cplx, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
                          ev_of(kPhaseSplit, true, true)));
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
 
     // Step 3: one exact INT8 product per modulus, reduced mod p_l.
-    HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, T->mod,
+    HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, group, T->mod,
                             (int8_t *)(ws + L.planes), L, s, ev_of(kPhaseGemm, true, true)));
 
     // Steps 4 + 5: reconstruction and unscaling.
-    HIP_TRY(launch_crt(el, (const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
-                       ev_of(kPhaseCrt, true, true)));
+    if (cplx)
+        HIP_TRY(launch_crt_complex(el, (const int8_t *)(ws + L.planes), m, n, e, f, T->crt, T->mod, C, ldc, L, s,
+                                   ev_of(kPhaseCrt, true, true)));
+    else
+        HIP_TRY(launch_crt(el, (const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
+                           ev_of(kPhaseCrt, true, true)));
 
     if (dbg) {
         if (dbg->e) HIP_TRY(hipMemcpyAsync(dbg->e, e, 4 * (size_t)m, hipMemcpyDeviceToDevice, s));
         if (dbg->f) HIP_TRY(hipMemcpyAsync(dbg->f, f, 4 * (size_t)n, hipMemcpyDeviceToDevice, s));
         if (dbg->ra)
-            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.ra), nmod, m, k, L.m_pad, L, dbg->ra, s));
+            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.ra), nmod * group, m, k, L.m_pad, L, dbg->ra, s));
         if (dbg->rb)
-            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.rb), nmod, n, k, L.n_pad, L, dbg->rb, s));
+            HIP_TRY(launch_unpack_residues((const int8_t *)(ws + L.rb), nmod * group, n, k, L.n_pad, L, dbg->rb, s));
         if (dbg->red)
-            HIP_TRY(launch_copy_planes_u8((const int8_t *)(ws + L.planes), nmod, T->mod, m, n, L, dbg->red, s));
+            HIP_TRY(launch_copy_planes_u8((const int8_t *)(ws + L.planes), nmod, group, T->mod, m, n, L, dbg->red,
+                                          s));
         if (dbg->prod) {
-            HIP_TRY(launch_gemm_raw((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod,
+            HIP_TRY(launch_gemm_raw((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, group,
                                     (int32_t *)(ws + L.raw), L, s));
-            HIP_TRY(launch_copy_planes_i32((const int32_t *)(ws + L.raw), nmod, m, n, L, dbg->prod, s));
+            HIP_TRY(launch_copy_planes_i32((const int32_t *)(ws + L.raw), nmod * group, m, n, L, dbg->prod, s));
         }
     }
     return OZAKI2_SUCCESS;
 }
 
 // Common front end of the product entry points.
-int front(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
-          void *C, int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, bool use_cache,
+int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B,
+          int64_t ldb, void *C, int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, bool use_cache,
           const DebugOut *dbg, void *stream) {
     int st = validate(m, n, k, A, lda, B, ldb, C, ldc, nmod, mode);
     if (st) return st;
     if (!layout_fits(m, n, k, mode)) return OZAKI2_ERR_UNSUPPORTED;
+    if (cplx && mode != OZAKI2_FAST) return OZAKI2_ERR_UNSUPPORTED;
     if (dbg && dbg->prod && k >= (1 << 17)) return OZAKI2_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     if (m == 0 || n == 0) return OZAKI2_SUCCESS;
     if (k == 0) {
-        HIP_TRY(launch_zero_fill(el, C, m, n, ldc, s));
+        // a complex column is 2m values with stride 2*ldc
+        HIP_TRY(launch_zero_fill(el, C, cplx ? 2 * m : m, n, cplx ? 2 * ldc : ldc, s));
         return OZAKI2_SUCCESS;
     }
-    const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr);
+    const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr, cplx ? 3 : 1);
     if (!use_cache) {
         if (workspace == nullptr) return -12;
         if (wbytes < L.total) return OZAKI2_ERR_WORKSPACE;
-        return run(el, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
+        return run(el, cplx, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
     }
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -264,7 +275,7 @@ int front(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, 
         g_cache.ptr[dev] = p;
         g_cache.bytes[dev] = L.total;
     }
-    return run(el, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
+    return run(el, cplx, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
 }
 
 }  // namespace
@@ -276,7 +287,8 @@ extern "C" {
 
 int ozaki2_dgemm(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
                  double *C, int64_t ldc, int num_moduli, int mode, void *stream) {
-    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
+    return front(Elem::f64, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr,
+                 stream);
 }
 
 size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode) {
@@ -298,8 +310,8 @@ size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_modu
 int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
                     double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                     void *stream) {
-    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false,
-                 nullptr, stream);
+    return front(Elem::f64, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, nullptr, stream);
 }
 
 int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
@@ -307,20 +319,21 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
     DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
-    return front(Elem::f64, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d,
-                 stream);
+    return front(Elem::f64, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, &d, stream);
 }
 
 int ozaki2_sgemm(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
                  float *C, int64_t ldc, int num_moduli, int mode, void *stream) {
-    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr, stream);
+    return front(Elem::f32, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr,
+                 stream);
 }
 
 int ozaki2_sgemm_ws(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
                     float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                     void *stream) {
-    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false,
-                 nullptr, stream);
+    return front(Elem::f32, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, nullptr, stream);
 }
 
 int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
@@ -328,8 +341,8 @@ int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t 
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
     DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
-    return front(Elem::f32, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, false, &d,
-                 stream);
+    return front(Elem::f32, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, &d, stream);
 }
 
 int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
@@ -355,6 +368,58 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
     HIP_TRY(launch_pack_planes(residues, num_moduli, T->mod, m, n, L, planes, s));
     HIP_TRY(launch_crt(Elem::f64, planes, m, n, e, f, T->crt, C, ldc, L, s));
     return OZAKI2_SUCCESS;
+}
+
+int ozaki2_zgemm(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                 double *C, int64_t ldc, int num_moduli, int mode, void *stream) {
+    return front(Elem::f64, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr,
+                 stream);
+}
+
+int ozaki2_zgemm_ws(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                    double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return front(Elem::f64, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, nullptr, stream);
+}
+
+int ozaki2_zgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
+                       uint8_t *red_out, void *stream) {
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    return front(Elem::f64, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, &d, stream);
+}
+
+int ozaki2_cgemm(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                 float *C, int64_t ldc, int num_moduli, int mode, void *stream) {
+    return front(Elem::f32, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr,
+                 stream);
+}
+
+int ozaki2_cgemm_ws(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    return front(Elem::f32, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, nullptr, stream);
+}
+
+int ozaki2_cgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t lda, const float *B, int64_t ldb,
+                       float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                       int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
+                       uint8_t *red_out, void *stream) {
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    return front(Elem::f32, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, &d, stream);
+}
+
+size_t ozaki2_zgemm_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int debug) {
+    if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
+                 m > 1 ? m : 1, num_moduli, OZAKI2_FAST))
+        return 0;
+    if (!layout_fits(m, n, k, OZAKI2_FAST) || m == 0 || n == 0 || k == 0) return 0;
+    return make_layout(m, n, k, num_moduli, OZAKI2_FAST, debug != 0, 3).total;
 }
 
 int ozaki2_max_moduli(void) { return kMaxModuli; }

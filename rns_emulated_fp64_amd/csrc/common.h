@@ -85,19 +85,21 @@ struct Ev {
 enum class Elem { f64, f32 };
 
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
-hipError_t launch_scale(Elem el, const void *A, int64_t m, int64_t k, int64_t lda, const void *B, int64_t n,
-                        int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
+// cplx: interleaved complex operands (A, B, C hold (re, im) pairs; leading
+// dimensions count complex elements).
+hipError_t launch_scale(Elem el, bool cplx, const void *A, int64_t m, int64_t k, int64_t lda, const void *B,
+                        int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_split(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
-                        int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L,
-                        char *ws, hipStream_t s, Ev ev = {});
+hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t lda, const void *B, int64_t n,
+                        int64_t ldb, int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc,
+                        const Layout &L, char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_quantize(Elem el, const void *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
                            const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
                            hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
-hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc,
+hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int group, const ModConsts &mc,
                            int8_t *planes, const Layout &L, hipStream_t s, Ev ev = {});
-hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw,
+hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int group, int32_t *raw,
                            const Layout &L, hipStream_t s);
 hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
                              const Layout &L, hipStream_t s);
@@ -105,11 +107,14 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
                                      hipStream_t s, Ev ev = {});
 hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, void *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev = {});
+hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e,
+                              const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
+                              const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_zero_fill(Elem el, void *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
 hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
-hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,
-                                 const Layout &L, uint8_t *out, hipStream_t s);
+hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, int group, const ModConsts &mc, int64_t m,
+                                 int64_t n, const Layout &L, uint8_t *out, hipStream_t s);
 hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
                               const Layout &L, int8_t *planes, hipStream_t s);
 hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,

@@ -15,6 +15,7 @@
 // own unless an fma() is written out, which the exact integer arithmetic
 // relies on.
 #include <float.h>
+#include <type_traits>
 #include <math.h>
 
 #include "common.h"
@@ -84,7 +85,7 @@ __device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
 // each thread accumulates every 4th column of its chunk, and the 4 lanes of a
 // row are merged in a fixed order through LDS. Output: one partial
 // (s, g, nonfinite) per (chunk, row).
-template <class T>
+template <class T, int W>
 __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                 int64_t kchunk, double *__restrict__ ps, int *__restrict__ pg,
                                                 int *__restrict__ pbad, int64_t rowblock, int64_t chunk) {
@@ -99,24 +100,32 @@ __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t
     int g = kExpEmpty;
     int bad = 0;
     if (i < m) {
-        const T *a = A + i;
+        // element (i, h) part c at A[(i + h*lda)*W + c]
+        const T *a = A + i * W;
+        const int64_t cs = lda * W;
         int64_t h = h0 + kl;
         for (; h + 28 < h1; h += 32) {
-            double v[8];
+            double v[8][W];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = (double)a[(h + 4 * u) * lda];
+            for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                double x = fabs(v[u]);
+                for (int c = 0; c < W; ++c) v[u][c] = (double)a[(h + 4 * u) * cs + c];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int c = 0; c < W; ++c) {
+                    double x = fabs(v[u][c]);
+                    if (!(x <= DBL_MAX)) bad = 1;
+                    else ssq_add(s, g, x);
+                }
+        }
+        for (; h < h1; h += 4)
+#pragma unroll
+            for (int c = 0; c < W; ++c) {
+                double x = fabs((double)a[h * cs + c]);
                 if (!(x <= DBL_MAX)) bad = 1;
                 else ssq_add(s, g, x);
             }
-        }
-        for (; h < h1; h += 4) {
-            double x = fabs((double)a[h * lda]);
-            if (!(x <= DBL_MAX)) bad = 1;
-            else ssq_add(s, g, x);
-        }
     }
     sh_s[kl][r] = s;
     sh_g[kl][r] = g;
@@ -252,8 +261,10 @@ __device__ __forceinline__ void col_exponents_block(const T *__restrict__ B, int
 }
 
 // Step 1 for both operands in one launch: blocks [0, nA) are row-norm blocks
-// of A (row block fastest, then k-chunk), the rest column blocks of B.
-template <class T>
+// of A (row block fastest, then k-chunk), the rest column blocks of B. W = 2:
+// complex operands with interleaved parts; a row's (column's) squared norm is
+// the sum over both parts, and a column of B is then 2k contiguous values.
+template <class T, int W>
 __global__ __launch_bounds__(256) void k_scale(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                int64_t kchunk, int64_t rowblocks, int64_t nA,
                                                double *__restrict__ ps, int *__restrict__ pg,
@@ -262,9 +273,9 @@ __global__ __launch_bounds__(256) void k_scale(const T *__restrict__ A, int64_t 
                                                int32_t *__restrict__ gb) {
     const int64_t bid = blockIdx.x;
     if (bid < nA)
-        row_norms_block(A, m, k, lda, kchunk, ps, pg, pbad, bid % rowblocks, bid / rowblocks);
+        row_norms_block<T, W>(A, m, k, lda, kchunk, ps, pg, pbad, bid % rowblocks, bid / rowblocks);
     else
-        col_exponents_block(B, k, n, n_pad, ldb, Pp, f, gb, bid - nA);
+        col_exponents_block(B, k * W, n, n_pad, ldb * W, Pp, f, gb, bid - nA);
 }
 
 // Accurate mode: e_i = floor(P' + 6 - r_i - 0.5 (log2 R_i + 4 u32)) with R_i
@@ -304,7 +315,8 @@ __global__ __launch_bounds__(256) void k_accurate_exponents(const int32_t *__res
 // the 16 bytes lane (t%64) holds in the packed layout.
 constexpr int kSplitRows = 32, kSplitCols = 128, kSplitLd = kSplitCols + 2;
 
-template <bool KCONTIG, class T>
+// W parts per element (1 real, 2 complex interleaved); X points at the part.
+template <bool KCONTIG, class T, int W = 1>
 __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const T *__restrict__ X,
                                                 int64_t rows, int64_t kdim, int64_t ld, int64_t r0,
                                                 int64_t h0) {
@@ -321,7 +333,7 @@ __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const 
         for (int it = 0; it < 16; ++it) {
             const int64_t h = h0 + hh + 8 * it;
             const bool ok = rok && h < kdim;
-            const double x = (double)X[rc + (ok ? h : 0) * ld];
+            const double x = (double)X[(rc + (ok ? h : 0) * ld) * W];
             v[it] = ok ? x : 0.0;
         }
 #pragma unroll
@@ -334,8 +346,8 @@ __device__ __forceinline__ void split_load_tile(double (*tile)[kSplitLd], const 
             const int64_t r = r0 + rq + 4 * it;
             const bool rok = r < rows;
             const bool ok0 = rok && h < kdim, ok1 = rok && h + 1 < kdim;
-            const T *row = X + (rok ? r : 0) * ld;
-            const double x0 = (double)row[ok0 ? h : 0], x1 = (double)row[ok1 ? h + 1 : 0];
+            const T *row = X + (rok ? r : 0) * ld * W;
+            const double x0 = (double)row[(ok0 ? h : 0) * W], x1 = (double)row[(ok1 ? h + 1 : 0) * W];
             v[2 * it] = ok0 ? x0 : 0.0;
             v[2 * it + 1] = ok1 ? x1 : 0.0;
         }
@@ -419,12 +431,73 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
     }
 }
 
+// The complex form of split_block: the real and imaginary tiles are staged
+// side by side, and each modulus l gets three planes, 3l + 0: residues of
+// trunc(2^e re), 3l + 1: of trunc(2^e im), 3l + 2: of their sum (reduced to
+// the symmetric range again), the operands of the three products of Gauss'
+// trick. Eight elements per pass keep the live splits small.
+template <bool KCONTIG, class T, class ExpOf>
+__device__ __forceinline__ void split_block_c(double (*tile)[kSplitRows][kSplitLd], const T *__restrict__ X,
+                                              int64_t rows, int64_t kdim, int64_t ld, ExpOf ex_row,
+                                              const SplitConsts &sc, int8_t *__restrict__ out, int64_t plane_bytes,
+                                              int64_t kb, int64_t bx, int64_t by) {
+    const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
+    split_load_tile<KCONTIG, T, 2>(tile[0], X, rows, kdim, ld, r0, h0);
+    split_load_tile<KCONTIG, T, 2>(tile[1], X + 1, rows, kdim, ld, r0, h0);
+    __syncthreads();
+
+    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
+    const int kk0 = fb * 32 + 16 * (lane >> 5);
+    const int64_t r = r0 + rr;
+    int e = r < rows ? ex_row(rr) : 0;
+    const bool zero = (e == kExpNonfinite);
+    if (zero) e = 0;
+    int8_t *dst = out + (bx * kb + by * 4 + fb) * 1024 + lane * 16;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+        // exact splits x = d1*2^42 + d0 of both parts (as in split_block)
+        double d0[2][8], d1[2][8];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                double a = zero ? 0.0 : tile[c][rr][kk0 + 8 * half + u];
+                double x = trunc(ldexp(a, e));
+                double hi = trunc(x * 0x1p-42);
+                d1[c][u] = hi;
+                d0[c][u] = fma(-hi, 0x1p42, x);
+            }
+        for (int l = 0; l < sc.n; ++l) {
+            const double p = sc.p[l], pinv = sc.pinv[l], c42 = sc.c42[l];
+            int v[3][8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    // p = 256: c42 = 0 and y = d0
+                    double y = fma(d1[c][u], c42, d0[c][u]);
+                    v[c][u] = (int)fma(-p, rint(y * pinv), y);
+                }
+                const double y = (double)(v[0][u] + v[1][u]);
+                v[2][u] = (int)fma(-p, rint(y * pinv), y);
+            }
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                uint2 w;
+                w.x = pack4(v[c][0], v[c][1], v[c][2], v[c][3]);
+                w.y = pack4(v[c][4], v[c][5], v[c][6], v[c][7]);
+                *(uint2 *)(dst + (3 * l + c) * plane_bytes + 8 * half) = w;
+            }
+        }
+    }
+}
+
 // Steps 1 + 2 for both operands in one launch: blocks [0, nA) split A (row
 // tile fastest, then K tile), the rest split B. FOLD: fast mode, where the
 // exponents of A's rows are merged here from the row-norm partials (the first
 // K tile of each row tile also stores them for the reconstruction); otherwise
 // they are read from e.
-template <bool FOLD, class T>
+template <bool FOLD, class T, int W>
 __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t m, int64_t lda,
                                                const T *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
                                                int64_t tilesA, int64_t tilesB, int64_t nA,
@@ -434,9 +507,17 @@ __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t 
                                                const int32_t *__restrict__ f, SplitConsts sc,
                                                int8_t *__restrict__ RA, int64_t planeA, int8_t *__restrict__ RB,
                                                int64_t planeB, int64_t kb) {
-    __shared__ double tile[kSplitRows][kSplitLd];
+    __shared__ double tile[W][kSplitRows][kSplitLd];
     __shared__ int sh_e[kSplitRows];
     const int64_t bid = blockIdx.x;
+    auto split_tile = [&](auto kcontig, const T *X, int64_t rows, int64_t ld, auto ex_row, int8_t *out,
+                          int64_t plane, int64_t bx, int64_t by) {
+        constexpr bool KC = decltype(kcontig)::value;
+        if constexpr (W == 2)
+            split_block_c<KC, T>(tile, X, rows, kdim, ld, ex_row, sc, out, plane, kb, bx, by);
+        else
+            split_block<KC, T>(tile[0], X, rows, kdim, ld, ex_row, sc, out, plane, kb, bx, by);
+    };
     if (bid < nA) {
         const int64_t bx = bid % tilesA, by = bid / tilesA;
         if (FOLD) {
@@ -447,18 +528,17 @@ __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t 
                 sh_e[threadIdx.x] = ev;
                 if (by == 0) e[i] = ev;  // i < m_pad: the workspace holds m_pad entries
             }
-            // split_block's barrier after the tile load orders these LDS writes
-            split_block<false, T>(tile, A, m, kdim, lda, [&](int rr) { return sh_e[rr]; }, sc, RA, planeA, kb, bx, by);
+            // the barrier after the tile load orders these LDS writes
+            split_tile(std::false_type{}, A, m, lda, [&](int rr) { return sh_e[rr]; }, RA, planeA, bx, by);
         } else {
             const int32_t *er = e + bx * kSplitRows;
-            split_block<false, T>(tile, A, m, kdim, lda, [&](int rr) { return (int)er[rr]; }, sc, RA, planeA, kb, bx,
-                               by);
+            split_tile(std::false_type{}, A, m, lda, [&](int rr) { return (int)er[rr]; }, RA, planeA, bx, by);
         }
     } else {
         const int64_t b = bid - nA;
         const int64_t bx = b % tilesB, by = b / tilesB;
         const int32_t *fr = f + bx * kSplitRows;
-        split_block<true, T>(tile, B, n, kdim, ldb, [&](int rr) { return (int)fr[rr]; }, sc, RB, planeB, kb, bx, by);
+        split_tile(std::true_type{}, B, n, ldb, [&](int rr) { return (int)fr[rr]; }, RB, planeB, bx, by);
     }
 }
 
@@ -526,7 +606,8 @@ struct GemmArgs {
     const int8_t *RB;
     int64_t planeA, planeB;  // bytes per modulus of RA, RB
     int64_t kb;              // K / 32
-    int tiles_m, tiles_n, nmod;
+    int tiles_m, tiles_n, nmod;  // nmod: operand/output planes (moduli x group)
+    int group;                   // planes per modulus: 1 (real) or 3 (complex)
     int64_t m_pad;
     // epilogues
     int8_t *planes;          // EPI_MOD: [nmod][n_pad][m_pad], symmetric residues
@@ -667,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // Inner dimension in blocks ([Q] step 3): after 2047 stages
             // (131008 terms of at most 2^14) fold the sums back to their
             // symmetric residues, so they never leave int32.
-            const double p = mc.p[l], pinv = mc.pinv[l];
+            const double p = mc.p[l / ga.group], pinv = mc.pinv[l / ga.group];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -684,7 +765,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int row_base = tm * kTileM + wm * 128 + 4 * (lane >> 5);
     const int col_base = tn * kTileN + wn * 128 + (lane & 31);
     if (EPI == EPI_MOD) {
-        const double p = mc.p[l], pinv = mc.pinv[l];
+        const double p = mc.p[l / ga.group], pinv = mc.pinv[l / ga.group];
         int8_t *plane = ga.planes + (int64_t)l * ga.plane_elems;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1032,6 +1113,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
     }
 }
 
+// Complex products: per modulus the planes 3l, 3l+1, 3l+2 hold T1 = re*re,
+// T2 = im*im and T3 = (re+im)*(re+im) mod p; the real part is T1 - T2 and the
+// imaginary part T3 - T1 - T2 (Gauss' trick, exact in residues). Each is
+// brought back to the symmetric range and both sums are accumulated in the
+// 40-bit pieces of k_crt (|c| <= 128 keeps every bound of that kernel), then
+// lifted and rounded like a real entry. C holds interleaved (re, im) pairs.
+template <class OutT>
+__global__ __launch_bounds__(256) void k_crt_c(const int8_t *__restrict__ planes, int64_t plane_elems,
+                                               int64_t m_pad, int64_t m, int64_t n, const int32_t *__restrict__ e,
+                                               const int32_t *__restrict__ f, CrtConsts cc, ModConsts mc,
+                                               OutT *__restrict__ C, int64_t ldc) {
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * kCrtRows;
+    if (i0 >= m) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i0;
+        double Sr[kCrtRows][4], Si[kCrtRows][4];
+#pragma unroll
+        for (int u = 0; u < kCrtRows; ++u)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) Sr[u][t] = Si[u][t] = 0.0;
+#pragma unroll 1
+        for (int l = 0; l < cc.n; ++l) {
+            const int32_t w1 = *(const int32_t *)(src + (int64_t)(3 * l) * plane_elems);
+            const int32_t w2 = *(const int32_t *)(src + (int64_t)(3 * l + 1) * plane_elems);
+            const int32_t w3 = *(const int32_t *)(src + (int64_t)(3 * l + 2) * plane_elems);
+            const double p = mc.p[l], pinv = mc.pinv[l];
+            const double W0 = cc.w[l][0], W1 = cc.w[l][1], W2 = cc.w[l][2], W3 = cc.w[l][3];
+#pragma unroll
+            for (int u = 0; u < kCrtRows; ++u) {
+                const int t1 = (w1 << (24 - 8 * u)) >> 24, t2 = (w2 << (24 - 8 * u)) >> 24,
+                          t3 = (w3 << (24 - 8 * u)) >> 24;
+                const double yr = (double)(t1 - t2), yi = (double)(t3 - t1 - t2);
+                const double cr = fma(-p, rint(yr * pinv), yr), ci = fma(-p, rint(yi * pinv), yi);
+                Sr[u][0] = fma(cr, W0, Sr[u][0]);
+                Sr[u][1] = fma(cr, W1, Sr[u][1]);
+                Sr[u][2] = fma(cr, W2, Sr[u][2]);
+                Sr[u][3] = fma(cr, W3, Sr[u][3]);
+                Si[u][0] = fma(ci, W0, Si[u][0]);
+                Si[u][1] = fma(ci, W1, Si[u][1]);
+                Si[u][2] = fma(ci, W2, Si[u][2]);
+                Si[u][3] = fma(ci, W3, Si[u][3]);
+            }
+        }
+        const int fj = f[j];
+#pragma unroll
+        for (int u = 0; u < kCrtRows; ++u) {
+            const int64_t i = i0 + u;
+            if (i < m) {
+                const int ei = e[i];
+                C[2 * (i + j * ldc)] = crt_finish<OutT>(Sr[u], ei, fj, cc);
+                C[2 * (i + j * ldc) + 1] = crt_finish<OutT>(Si[u], ei, fj, cc);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
@@ -1070,11 +1207,11 @@ __global__ void k_copy_planes_i32(const int32_t *planes, int64_t m, int64_t m_pa
 
 // symmetric residues -> [0, p)
 __global__ void k_copy_planes_red(const int8_t *planes, int64_t m, int64_t m_pad, int64_t plane_elems, int64_t n,
-                                  ModConsts mc, uint8_t *out) {
+                                  ModConsts mc, int group, uint8_t *out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t l = blockIdx.z;
     if (i >= m) return;
-    const int p = (int)mc.p[l];
+    const int p = (int)mc.p[l / group];
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
         int v = planes[l * plane_elems + j * m_pad + i];
         if (p == 256) v &= 0xff;
@@ -1103,23 +1240,28 @@ __global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t 
 static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count + per - 1) / per); }
 static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
 
-template <class T>
+template <class T, int W>
 static hipError_t launch_scale_t(const T *A, int64_t m, int64_t k, int64_t lda, const T *B, int64_t n, int64_t ldb,
                                  double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t rowblocks = (m + 63) / 64;
     const int64_t nA = rowblocks * L.nchunks, nB = L.n_pad / 4;
-    auto kern = k_scale<T>;
+    auto kern = k_scale<T, W>;
     OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, k, lda, L.kchunk, rowblocks, nA,
                (double *)(ws + L.part_s), (int *)(ws + L.part_g), (int *)(ws + L.part_bad), B, n, L.n_pad, ldb, Pp,
                (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
     return hipGetLastError();
 }
 
-hipError_t launch_scale(Elem el, const void *A, int64_t m, int64_t k, int64_t lda, const void *B, int64_t n,
-                        int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
-    if (el == Elem::f32)
-        return launch_scale_t((const float *)A, m, k, lda, (const float *)B, n, ldb, Pp, L, ws, s, ev);
-    return launch_scale_t((const double *)A, m, k, lda, (const double *)B, n, ldb, Pp, L, ws, s, ev);
+hipError_t launch_scale(Elem el, bool cplx, const void *A, int64_t m, int64_t k, int64_t lda, const void *B,
+                        int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+    if (el == Elem::f32) {
+        const float *a = (const float *)A, *b = (const float *)B;
+        return cplx ? launch_scale_t<float, 2>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev)
+                    : launch_scale_t<float, 1>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
+    }
+    const double *a = (const double *)A, *b = (const double *)B;
+    return cplx ? launch_scale_t<double, 2>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev)
+                : launch_scale_t<double, 1>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
 }
 
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
@@ -1129,12 +1271,12 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
     return hipGetLastError();
 }
 
-template <bool FOLD, class T>
+template <bool FOLD, class T, int W>
 static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B, int64_t n, int64_t ldb, int64_t k,
                                  double Pp, const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows, tilesK = L.k_pad / kSplitCols;
     const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
-    auto kern = k_split<FOLD, T>;
+    auto kern = k_split<FOLD, T, W>;
     OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
                (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
                L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
@@ -1142,17 +1284,19 @@ static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B,
     return hipGetLastError();
 }
 
-hipError_t launch_split(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
-                        int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc, const Layout &L,
-                        char *ws, hipStream_t s, Ev ev) {
+hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t lda, const void *B, int64_t n,
+                        int64_t ldb, int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc,
+                        const Layout &L, char *ws, hipStream_t s, Ev ev) {
     if (el == Elem::f32) {
         const float *a = (const float *)A, *b = (const float *)B;
-        return fold_row_exponents ? launch_split_t<true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
-                                  : launch_split_t<false>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+        if (cplx) return launch_split_t<true, float, 2>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+        return fold_row_exponents ? launch_split_t<true, float, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
+                                  : launch_split_t<false, float, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
     }
     const double *a = (const double *)A, *b = (const double *)B;
-    return fold_row_exponents ? launch_split_t<true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
-                              : launch_split_t<false>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+    if (cplx) return launch_split_t<true, double, 2>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
+    return fold_row_exponents ? launch_split_t<true, double, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
+                              : launch_split_t<false, double, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
 }
 
 template <class T>
@@ -1180,7 +1324,7 @@ hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t
     return hipGetLastError();
 }
 
-static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, const Layout &L) {
+static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L) {
     GemmArgs g{};
     g.RA = RA;
     g.RB = RB;
@@ -1189,17 +1333,18 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, const La
     g.kb = L.kb;
     g.tiles_m = (int)(L.m_pad / kTileM);
     g.tiles_n = (int)(L.n_pad / kTileN);
-    g.nmod = nmod;
+    g.nmod = nmod * group;
+    g.group = group;
     g.m_pad = L.m_pad;
     g.plane_elems = L.m_pad * L.n_pad;
     return g;
 }
 
-hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const ModConsts &mc, int8_t *planes,
-                           const Layout &L, hipStream_t s, Ev ev) {
-    GemmArgs g = gemm_args(RA, RB, nmod, L);
+hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int group, const ModConsts &mc,
+                           int8_t *planes, const Layout &L, hipStream_t s, Ev ev) {
+    GemmArgs g = gemm_args(RA, RB, nmod, group, L);
     g.planes = planes;
-    const int blocks = g.tiles_m * g.tiles_n * nmod;
+    const int blocks = g.tiles_m * g.tiles_n * g.nmod;
     if (g.kb / kKS > kReduceStages) {
         auto kern = k_gemm<EPI_MOD, true>;
         OZ2_LAUNCH(ev, kern, dim3(blocks), dim3(256), 0, s, g, mc);
@@ -1210,19 +1355,19 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, const M
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int32_t *raw, const Layout &L,
+hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int group, int32_t *raw, const Layout &L,
                            hipStream_t s) {
-    GemmArgs g = gemm_args(RA, RB, nmod, L);
+    GemmArgs g = gemm_args(RA, RB, nmod, group, L);
     g.raw = raw;
     ModConsts mc{};
-    const int blocks = g.tiles_m * g.tiles_n * nmod;
+    const int blocks = g.tiles_m * g.tiles_n * g.nmod;
     hipLaunchKernelGGL((k_gemm<EPI_RAW, false>), dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
                              const Layout &L, hipStream_t s) {
-    GemmArgs g = gemm_args(Abar, Bbar, 1, L);
+    GemmArgs g = gemm_args(Abar, Bbar, 1, 1, L);
     g.rowmax = rowmax;
     g.colmax = colmax;
     ModConsts mc{};
@@ -1262,6 +1407,22 @@ hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const
     return launch_crt_t(planes, m, n, e, f, cc, (double *)C, ldc, L, s, ev);
 }
 
+hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e,
+                              const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
+                              const Layout &L, hipStream_t s, Ev ev) {
+    dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
+    if (el == Elem::f32) {
+        auto kern = k_crt_c<float>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, mc,
+                   (float *)C, ldc);
+    } else {
+        auto kern = k_crt_c<double>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, mc,
+                   (double *)C, ldc);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
                               const Layout &L, int8_t *planes, hipStream_t s) {
     dim3 grid(nblk(L.m_pad, 256), ydim(n), (unsigned)nmod);
@@ -1284,10 +1445,11 @@ hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, 
     return hipGetLastError();
 }
 
-hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, const ModConsts &mc, int64_t m, int64_t n,
-                                 const Layout &L, uint8_t *out, hipStream_t s) {
-    dim3 grid(nblk(m, 256), ydim(n), (unsigned)nmod);
-    hipLaunchKernelGGL(k_copy_planes_red, grid, dim3(256), 0, s, planes, m, L.m_pad, L.m_pad * L.n_pad, n, mc, out);
+hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, int group, const ModConsts &mc, int64_t m,
+                                 int64_t n, const Layout &L, uint8_t *out, hipStream_t s) {
+    dim3 grid(nblk(m, 256), ydim(n), (unsigned)(nmod * group));
+    hipLaunchKernelGGL(k_copy_planes_red, grid, dim3(256), 0, s, planes, m, L.m_pad, L.m_pad * L.n_pad, n, mc, group,
+                       out);
     return hipGetLastError();
 }
 

@@ -90,6 +90,21 @@ def test_status_codes(args, status):
     assert oz.ozaki2_sgemm_ws(*args, P, 1 << 40, 0) == status
 
 
+def test_complex_status_codes():
+    # same argument checks as the real entry points; accurate mode is not defined for complex products
+    for fn in (oz.ozaki2_zgemm, oz.ozaki2_cgemm):
+        assert fn(-1, 4, 4, P, 4, P, 4, P, 4, 8, 0, 0) == -1
+        assert fn(4, 4, 4, P, 3, P, 4, P, 4, 8, 0, 0) == -5
+        assert fn(4, 4, 4, P, 4, P, 4, P, 4, 21, 0, 0) == -10
+        assert fn(4, 4, 4, P, 4, P, 4, P, 4, 8, 1, 0) == 3
+        assert fn(0, 4, 4, 0, 1, P, 4, 0, 1, 8, 0, 0) == 0
+    assert oz.ozaki2_zgemm_ws(4, 4, 4, P, 4, P, 4, P, 4, 8, 0, 0, 0, 0) == -12
+    need = oz.ozaki2_zgemm_workspace_size(64, 64, 64, 8)
+    assert need > oz.ozaki2_workspace_size(64, 64, 64, 8, 0)
+    assert oz.ozaki2_zgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, P, need - 1, 0) == 2
+    assert oz.ozaki2_zgemm_workspace_size(64, 64, 64, 8, debug=True) > need
+
+
 def test_workspace_checks():
     assert oz.ozaki2_dgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, 0, 0, 0) == -12
     need = oz.ozaki2_workspace_size(64, 64, 64, 8, 0)
