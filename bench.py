@@ -240,6 +240,32 @@ def main():
             ms6 = time_steps(lambda: torch.mm(Ats, Bts), max(args.steps // 2, 3), 2, torch)
             extras["native_fp32_gemm_tflops"] = round(sflops / (ms6 * 1e-3) / 1e12, 3)
             del dAs, dBs, dCs, wss, Ats, Bts
+            # complex products (ZGEMM, Gauss' three products per modulus) on complex
+            # operands of the same spread at the same size; 8mnk real flops
+            rngz = np.random.default_rng(0)
+            Az = W.spread_matrix(rngz, (m, k), 1.0) + 1j * W.spread_matrix(rngz, (m, k), 1.0)
+            Bz = W.spread_matrix(rngz, (k, n), 1.0) + 1j * W.spread_matrix(rngz, (k, n), 1.0)
+            dAz = torch.from_numpy(np.ascontiguousarray(Az.T)).to(dev)  # column-major, interleaved
+            dBz = torch.from_numpy(np.ascontiguousarray(Bz.T)).to(dev)
+            dCz = torch.empty((n, m), dtype=torch.complex128, device=dev)
+            wbz = oz.ozaki2_zgemm_workspace_size(m, n, k, N)
+            wsz = torch.empty(wbz, dtype=torch.uint8, device=dev)
+
+            def zstep():
+                st = oz.ozaki2_zgemm_ws(m, n, k, dAz.data_ptr(), m, dBz.data_ptr(), k, dCz.data_ptr(), m, N, oz.FAST,
+                                        wsz.data_ptr(), wbz, stream)
+                if st:
+                    raise RuntimeError(oz.status_string(st))
+
+            ms7 = time_steps(zstep, max(args.steps // 2, 3), 2, torch)
+            extras[f"zgemm_n{N}_tflops"] = round(4 * flops / (ms7 * 1e-3) / 1e12, 3)
+            extras[f"zgemm_n{N}_ms_per_step"] = round(ms7, 4)
+            del wsz, dCz
+            Azt = torch.from_numpy(Az).to(dev)
+            Bzt = torch.from_numpy(Bz).to(dev)
+            ms8 = time_steps(lambda: torch.mm(Azt, Bzt), max(args.steps // 2, 3), 2, torch)
+            extras["native_complex128_gemm_tflops"] = round(4 * flops / (ms8 * 1e-3) / 1e12, 3)
+            del dAz, dBz, Azt, Bzt
         # the vendor INT8 GEMM (torch._int_mm = hipBLASLt) on random int8 of one
         # modulus' shape, as context for the INT8 roofline fraction
         try:
