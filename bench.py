@@ -110,6 +110,27 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
              **{f"native_{nat}_E_cw": native["E_cw"], f"native_{nat}_E_el": native["E_el"]})
 
 
+def cpu_baseline_complex(A, B, C_gpu, N, rows_wanted):
+    """The oracle's complex emulation on the first rows of A times all of B."""
+    import numpy as np
+    import oracle as O
+    m, k = A.shape
+    n = B.shape[1]
+    rows = min(m, rows_wanted or max(8, int(1024 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
+    log(f"cpu_baseline: complex oracle on {rows} rows x {n} columns, k={k}, N={N}")
+    t0 = time.perf_counter()
+    r = O.os2_zgemm(A[:rows], B, N)
+    t = time.perf_counter() - t0
+    Cs = C_gpu[:rows]
+    same = lambda x, y: (x.view(np.uint64) == y.view(np.uint64)) | (np.isnan(x) & np.isnan(y))
+    ok = same(np.ascontiguousarray(Cs.real), np.ascontiguousarray(r["C"].real)) & \
+        same(np.ascontiguousarray(Cs.imag), np.ascontiguousarray(r["C"].imag))
+    return dict(value=8.0 * rows * n * k / t / 1e12, unit="TFLOPS", cores=int(os.environ.get("OMP_NUM_THREADS",
+                os.cpu_count() or 1)), kind="oracle",
+                sample=f"rows 0..{rows - 1} of A times all of B ({rows}x{n}x{k} complex, N={N}); {t:.2f} s"), \
+        dict(parity_mismatches=int((~ok).sum()), parity_entries=int(Cs.size))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -140,18 +161,20 @@ def main():
         raise SystemExit("the scale sweep is a parity-test case, not a bench line")
     m, n, k, N = cfg["m"], cfg["n"], cfg["k"], cfg["num_moduli"]
     single = bool(cfg.get("single"))
+    cplx = bool(cfg.get("complex"))
     md = oz.MODES[args.mode]
     log(f"generating {args.config} ({m}x{k} @ {k}x{n}), N={N}, mode={args.mode}")
     A, B = W.make(args.config)
     dev = torch.device("cuda:0")
     dA = torch.from_numpy(np.ascontiguousarray(A.T)).to(dev)  # column-major A, lda = m
     dB = torch.from_numpy(np.ascontiguousarray(B.T)).to(dev)  # column-major B, ldb = k
-    dC = torch.empty((n, m), dtype=torch.float32 if single else torch.float64, device=dev)
-    gemm_ws = oz.ozaki2_sgemm_ws if single else oz.ozaki2_dgemm_ws
+    dC = torch.empty((n, m), dtype=torch.complex128 if cplx else torch.float32 if single else torch.float64,
+                     device=dev)
+    gemm_ws = oz.ozaki2_zgemm_ws if cplx else oz.ozaki2_sgemm_ws if single else oz.ozaki2_dgemm_ws
     stream = torch.cuda.current_stream(dev).cuda_stream
 
     def workspace(mode_id):
-        wb = oz.ozaki2_workspace_size(m, n, k, N, mode_id)
+        wb = oz.ozaki2_zgemm_workspace_size(m, n, k, N) if cplx else oz.ozaki2_workspace_size(m, n, k, N, mode_id)
         return torch.empty(wb, dtype=torch.uint8, device=dev), wb
 
     ws, wbytes = workspace(md)
@@ -188,9 +211,10 @@ def main():
     phase_avg = {p: v / max(pcalls, 1) for p, v in phase_ms.items()}
     log(f"{ms:.3f} ms/step; GEMM {gemm_avg:.4f} ms (timed region); phases {phase_avg}")
 
-    flops = 2.0 * m * n * k
+    flops = (8.0 if cplx else 2.0) * m * n * k  # a complex multiply-add is 8 real flops
     tflops = flops / (ms * 1e-3) / 1e12
-    int8_ops = N * flops  # one INT8 GEMM per modulus, all in one launch
+    # one INT8 GEMM per modulus (three for complex products), all in one launch
+    int8_ops = N * (3 if cplx else 1) * 2.0 * m * n * k
     gemm_tops = int8_ops / (gemm_avg * 1e-3) / 1e12
     traffic = gemm_traffic_bytes() if args.config == "spread1.0_4096_n16" and args.mode == "fast" else None
     roofline = dict(bound="mfma", achieved=round(gemm_tops, 2), peak=INT8_PEAK_TOPS, unit="TFLOP/s",
@@ -199,7 +223,13 @@ def main():
 
     C = dC.cpu().numpy().T  # C of the last step
     extras = {}
-    if not args.no_extras:
+    if cplx and not args.no_extras:
+        Azt = torch.from_numpy(A).to(dev)
+        Bzt = torch.from_numpy(B).to(dev)
+        ms8 = time_steps(lambda: torch.mm(Azt, Bzt), max(args.steps // 2, 3), 2, torch)
+        extras["native_complex128_gemm_tflops"] = round(flops / (ms8 * 1e-3) / 1e12, 3)
+        del Azt, Bzt
+    elif not args.no_extras:
         # accurate mode (the other mode) and native FP64 on the same operands, as context
         other = "accurate" if args.mode == "fast" else "fast"
         w2, wb2 = workspace(oz.MODES[other])
@@ -242,9 +272,7 @@ def main():
             del dAs, dBs, dCs, wss, Ats, Bts
             # complex products (ZGEMM, Gauss' three products per modulus) on complex
             # operands of the same spread at the same size; 8mnk real flops
-            rngz = np.random.default_rng(0)
-            Az = W.spread_matrix(rngz, (m, k), 1.0) + 1j * W.spread_matrix(rngz, (m, k), 1.0)
-            Bz = W.spread_matrix(rngz, (k, n), 1.0) + 1j * W.spread_matrix(rngz, (k, n), 1.0)
+            Az, Bz = W.make("zgemm_spread1.0_4096_n16")
             dAz = torch.from_numpy(np.ascontiguousarray(Az.T)).to(dev)  # column-major, interleaved
             dBz = torch.from_numpy(np.ascontiguousarray(Bz.T)).to(dev)
             dCz = torch.empty((n, m), dtype=torch.complex128, device=dev)
@@ -279,11 +307,13 @@ def main():
 
     cpu = None
     accuracy = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not cplx:
         cpu, accuracy = cpu_baseline_leg(A, B, C, N, args.mode, args.cpu_rows)
+    elif not args.no_cpu_baseline:
+        cpu, accuracy = cpu_baseline_complex(A, B, C, N, args.cpu_rows)
 
     line = dict(
-        metric=("emulated FP32 TFLOPS (2mnk/t)" if single else
+        metric=("emulated complex FP64 TFLOPS (8mnk/t)" if cplx else "emulated FP32 TFLOPS (2mnk/t)" if single else
                 "emulated FP64 TFLOPS (2mnk/t) at 4096^3, % INT8 MFMA peak; max rel err"),
         value=round(tflops, 3), unit="TFLOPS", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms, 4), higher_is_better=True, scaling="weak", vs_baseline=None,

@@ -431,63 +431,68 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
     }
 }
 
-// The complex form of split_block: the real and imaginary tiles are staged
-// side by side, and each modulus l gets three planes, 3l + 0: residues of
-// trunc(2^e re), 3l + 1: of trunc(2^e im), 3l + 2: of their sum (reduced to
-// the symmetric range again), the operands of the three products of Gauss'
-// trick. Eight elements per pass keep the live splits small.
+// The complex form of split_block, over rows [bx*32, +32) x K [by*64, +64).
+// Each modulus l gets three planes, 3l + 0: residues of trunc(2^e re),
+// 3l + 1: of trunc(2^e im), 3l + 2: of their sum, the operands of the three
+// products of Gauss' trick. The sum's residue comes from the exact splits:
+// (d1r + d1i) 2^42 + (d0r + d0i) is the sum with |d0r + d0i| < 2^43, so
+// y = (d1r + d1i)(2^42 mod p) + (d0r + d0i) stays below 2^50.2 and exact.
+// Thread pairs share a lane's 16 bytes (8 K each), so every store of a
+// wavefront covers 512 contiguous bytes. Elements are loaded straight from
+// memory (for A, 32 lanes read 32 consecutive complex rows at one k; for B
+// each thread reads 8 consecutive complex k): no LDS tile.
+constexpr int kSplitColsC = 64;
 template <bool KCONTIG, class T, class ExpOf>
-__device__ __forceinline__ void split_block_c(double (*tile)[kSplitRows][kSplitLd], const T *__restrict__ X,
-                                              int64_t rows, int64_t kdim, int64_t ld, ExpOf ex_row,
-                                              const SplitConsts &sc, int8_t *__restrict__ out, int64_t plane_bytes,
-                                              int64_t kb, int64_t bx, int64_t by) {
-    const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
-    split_load_tile<KCONTIG, T, 2>(tile[0], X, rows, kdim, ld, r0, h0);
-    split_load_tile<KCONTIG, T, 2>(tile[1], X + 1, rows, kdim, ld, r0, h0);
+__device__ __forceinline__ void split_block_c(const T *__restrict__ X, int64_t rows, int64_t kdim, int64_t ld,
+                                              ExpOf ex_row, const SplitConsts &sc, int8_t *__restrict__ out,
+                                              int64_t plane_bytes, int64_t kb, int64_t bx, int64_t by) {
+    const int t = threadIdx.x, fb = t >> 7, q = t & 127, lane = q >> 1, half = q & 1, rr = lane & 31;
+    const int64_t r = bx * kSplitRows + rr;
+    const int64_t k0 = by * kSplitColsC + fb * 32 + 16 * (lane >> 5) + 8 * half;
+    const bool rok = r < rows;
+    const int64_t rc = rok ? r : 0;
+    double x[2][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int64_t h = k0 + u;
+        const bool ok = rok && h < kdim;
+        const int64_t idx = KCONTIG ? (ok ? h : 0) + rc * ld : rc + (ok ? h : 0) * ld;
+        const T re = X[2 * idx], im = X[2 * idx + 1];
+        x[0][u] = ok ? (double)re : 0.0;
+        x[1][u] = ok ? (double)im : 0.0;
+    }
+    // row exponents may come from LDS written before this call
     __syncthreads();
-
-    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
-    const int kk0 = fb * 32 + 16 * (lane >> 5);
-    const int64_t r = r0 + rr;
-    int e = r < rows ? ex_row(rr) : 0;
+    int e = rok ? ex_row(rr) : 0;
     const bool zero = (e == kExpNonfinite);
     if (zero) e = 0;
-    int8_t *dst = out + (bx * kb + by * 4 + fb) * 1024 + lane * 16;
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-        // exact splits x = d1*2^42 + d0 of both parts (as in split_block)
-        double d0[2][8], d1[2][8];
+    double d1[3][8], d0[3][8];  // exact splits of re, im and of their sum
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const double xs = zero ? 0.0 : trunc(ldexp(x[c][u], e));
+            d1[c][u] = trunc(xs * 0x1p-42);
+            d0[c][u] = fma(-d1[c][u], 0x1p42, xs);
+        }
+        d1[2][u] = d1[0][u] + d1[1][u];
+        d0[2][u] = d0[0][u] + d0[1][u];
+    }
+    int8_t *dst = out + (bx * kb + by * (kSplitColsC / 32) + fb) * 1024 + lane * 16 + 8 * half;
+    for (int l = 0; l < sc.n; ++l) {
+        const double p = sc.p[l], pinv = sc.pinv[l], c42 = sc.c42[l];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            int v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                double a = zero ? 0.0 : tile[c][rr][kk0 + 8 * half + u];
-                double x = trunc(ldexp(a, e));
-                double hi = trunc(x * 0x1p-42);
-                d1[c][u] = hi;
-                d0[c][u] = fma(-hi, 0x1p42, x);
+                const double y = fma(d1[c][u], c42, d0[c][u]);  // p = 256: c42 = 0
+                v[u] = (int)fma(-p, rint(y * pinv), y);
             }
-        for (int l = 0; l < sc.n; ++l) {
-            const double p = sc.p[l], pinv = sc.pinv[l], c42 = sc.c42[l];
-            int v[3][8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    // p = 256: c42 = 0 and y = d0
-                    double y = fma(d1[c][u], c42, d0[c][u]);
-                    v[c][u] = (int)fma(-p, rint(y * pinv), y);
-                }
-                const double y = (double)(v[0][u] + v[1][u]);
-                v[2][u] = (int)fma(-p, rint(y * pinv), y);
-            }
-#pragma unroll
-            for (int c = 0; c < 3; ++c) {
-                uint2 w;
-                w.x = pack4(v[c][0], v[c][1], v[c][2], v[c][3]);
-                w.y = pack4(v[c][4], v[c][5], v[c][6], v[c][7]);
-                *(uint2 *)(dst + (3 * l + c) * plane_bytes + 8 * half) = w;
-            }
+            uint2 w;
+            w.x = pack4(v[0], v[1], v[2], v[3]);
+            w.y = pack4(v[4], v[5], v[6], v[7]);
+            *(uint2 *)(dst + (3 * l + c) * plane_bytes) = w;
         }
     }
 }
@@ -507,14 +512,14 @@ __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t 
                                                const int32_t *__restrict__ f, SplitConsts sc,
                                                int8_t *__restrict__ RA, int64_t planeA, int8_t *__restrict__ RB,
                                                int64_t planeB, int64_t kb) {
-    __shared__ double tile[W][kSplitRows][kSplitLd];
+    __shared__ double tile[W == 1 ? 1 : 0 + 1][W == 1 ? kSplitRows : 1][W == 1 ? kSplitLd : 1];
     __shared__ int sh_e[kSplitRows];
     const int64_t bid = blockIdx.x;
     auto split_tile = [&](auto kcontig, const T *X, int64_t rows, int64_t ld, auto ex_row, int8_t *out,
                           int64_t plane, int64_t bx, int64_t by) {
         constexpr bool KC = decltype(kcontig)::value;
         if constexpr (W == 2)
-            split_block_c<KC, T>(tile, X, rows, kdim, ld, ex_row, sc, out, plane, kb, bx, by);
+            split_block_c<KC, T>(X, rows, kdim, ld, ex_row, sc, out, plane, kb, bx, by);
         else
             split_block<KC, T>(tile[0], X, rows, kdim, ld, ex_row, sc, out, plane, kb, bx, by);
     };
@@ -1274,7 +1279,8 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
 template <bool FOLD, class T, int W>
 static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B, int64_t n, int64_t ldb, int64_t k,
                                  double Pp, const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev) {
-    const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows, tilesK = L.k_pad / kSplitCols;
+    const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows;
+    const int64_t tilesK = L.k_pad / (W == 2 ? kSplitColsC : kSplitCols);
     const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
     auto kern = k_split<FOLD, T, W>;
     OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,

@@ -84,13 +84,27 @@ CONFIGS = {
     # to binary32, N=8.
     "sgemm_spread1.0_4096_n8": dict(m=4096, n=4096, k=4096, num_moduli=8, kind="spread", phi=1.0, seed=0,
                                     single=True),
+    # Complex products ("Improved Scaling ...", closing remark: ZGEMM/CGEMM):
+    # real and imaginary parts drawn like the phi=1.0 workload at 4096^3, N=16.
+    "zgemm_spread1.0_4096_n16": dict(m=4096, n=4096, k=4096, num_moduli=16, kind="spread", phi=1.0, seed=0,
+                                     complex=True),
 }
+
+
+def complex_spread_case(m: int, n: int, k: int, phi: float, seed: int = 0):
+    """Complex A, B: Re A, Im A, Re B, Im B drawn in that order as spread_matrix."""
+    rng = np.random.default_rng(seed)
+    ar, ai = spread_matrix(rng, (m, k), phi), spread_matrix(rng, (m, k), phi)
+    br, bi = spread_matrix(rng, (k, n), phi), spread_matrix(rng, (k, n), phi)
+    return ar + 1j * ai, br + 1j * bi
 
 
 def make(name: str):
     """Operands (A, B) of a named workload (not for the scale sweep); binary32
     arrays (the float64 draw rounded to nearest) for single-precision ones."""
     c = CONFIGS[name]
+    if c.get("complex"):
+        return complex_spread_case(c["m"], c["n"], c["k"], c["phi"], c["seed"])
     if c["kind"] == "uniform":
         a, b = uniform_case(c["m"], c["n"], c["k"], c["seed"])
     elif c["kind"] == "spread":
