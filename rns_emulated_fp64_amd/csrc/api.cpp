@@ -185,13 +185,8 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
     if (accurate) {
         // Accurate mode bounds the products with one extra INT8 GEMM first
         // ([G] Problemstellung).
-        HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));
-        HIP_TRY(launch_quantize(el, A, m, k, lda, false, (const int32_t *)(ws + L.ga), (int8_t *)(ws + L.abar),
-                                L.m_pad, L, s));
-        HIP_TRY(launch_quantize(el, B, n, k, ldb, true, (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.bbar),
-                                L.n_pad, L, s));
-        HIP_TRY(launch_fill_i32((int32_t *)(ws + L.rowmax), L.m_pad, 0, s));
-        HIP_TRY(launch_fill_i32((int32_t *)(ws + L.colmax), L.n_pad, 0, s));
+        HIP_TRY(launch_row_exponents(m, T->Pp, L, ws, s));  // also clears the row/column maxima
+        HIP_TRY(launch_quantize(el, A, m, lda, B, n, ldb, k, L, ws, s));
         HIP_TRY(launch_gemm_bound((const int8_t *)(ws + L.abar), (const int8_t *)(ws + L.bbar),
                                   (int32_t *)(ws + L.rowmax), (int32_t *)(ws + L.colmax), L, s));
         HIP_TRY(launch_accurate_exponents(m, n, T->Pp, L, ws, s, ev_of(kPhaseScale, false, true)));

@@ -93,10 +93,8 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
 hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t lda, const void *B, int64_t n,
                         int64_t ldb, int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc,
                         const Layout &L, char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_quantize(Elem el, const void *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
-                           hipStream_t s);
-hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
+hipError_t launch_quantize(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
+                           int64_t k, const Layout &L, char *ws, hipStream_t s);
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int group, const ModConsts &mc,
                            int8_t *planes, const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int group, int32_t *raw,

@@ -186,13 +186,17 @@ __device__ __forceinline__ void row_exponent_from_partials(const double *__restr
 }
 
 // Row exponents of every row from the chunk partials (accurate mode, which
-// needs them before the bound product). Rows in [m, m_pad) get 0.
+// needs them before the bound product). Rows in [m, m_pad) get 0. The same
+// threads clear the row and column maxima the bound product accumulates.
 __global__ __launch_bounds__(256) void k_row_exponents(const double *__restrict__ ps, const int *__restrict__ pg,
                                                        const int *__restrict__ pbad, int64_t m, int64_t m_pad,
                                                        int nchunks, double Pp, int32_t *__restrict__ e,
-                                                       int32_t *__restrict__ ga) {
+                                                       int32_t *__restrict__ ga, int32_t *__restrict__ rowmax,
+                                                       int32_t *__restrict__ colmax, int64_t n_pad) {
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n_pad) colmax[i] = 0;
     if (i >= m_pad) return;
+    rowmax[i] = 0;
     int ev = 0, gv = 0;
     if (i < m) row_exponent_from_partials(ps, pg, pbad, m, i, nchunks, Pp, ev, gv);
     e[i] = ev;
@@ -549,11 +553,10 @@ __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t 
 
 // Accurate mode: Abar_ih = ceil(|a_ih| * 2^(6 - r_i)) in [0, 64], same packing.
 template <bool KCONTIG, class T>
-__global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ X, int64_t rows, int64_t kdim,
-                                                  int64_t ld, const int32_t *__restrict__ gx,
-                                                  int8_t *__restrict__ out, int64_t kb) {
-    __shared__ double tile[kSplitRows][kSplitLd];
-    const int64_t r0 = (int64_t)blockIdx.x * kSplitRows, h0 = (int64_t)blockIdx.y * kSplitCols;
+__device__ __forceinline__ void quantize_block(double (*tile)[kSplitLd], const T *__restrict__ X, int64_t rows,
+                                               int64_t kdim, int64_t ld, const int32_t *__restrict__ gx,
+                                               int8_t *__restrict__ out, int64_t kb, int64_t bx, int64_t by) {
+    const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
     split_load_tile<KCONTIG, T>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
     const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
@@ -573,7 +576,25 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ X, int64
     w.y = pack4(v[4], v[5], v[6], v[7]);
     w.z = pack4(v[8], v[9], v[10], v[11]);
     w.w = pack4(v[12], v[13], v[14], v[15]);
-    *(uint4 *)(out + ((int64_t)blockIdx.x * kb + (int64_t)blockIdx.y * 4 + fb) * 1024 + lane * 16) = w;
+    *(uint4 *)(out + (bx * kb + by * 4 + fb) * 1024 + lane * 16) = w;
+}
+
+// Both bound operands in one launch: blocks [0, nA) quantize A (row tile
+// fastest, then K tile), the rest B.
+template <class T>
+__global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64_t m, int64_t lda,
+                                                  const T *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
+                                                  int64_t tilesA, int64_t tilesB, int64_t nA,
+                                                  const int32_t *__restrict__ ga, const int32_t *__restrict__ gb,
+                                                  int8_t *__restrict__ abar, int8_t *__restrict__ bbar, int64_t kb) {
+    __shared__ double tile[kSplitRows][kSplitLd];
+    const int64_t bid = blockIdx.x;
+    if (bid < nA) {
+        quantize_block<false, T>(tile, A, m, kdim, lda, ga, abar, kb, bid % tilesA, bid / tilesA);
+    } else {
+        const int64_t b = bid - nA;
+        quantize_block<true, T>(tile, B, n, kdim, ldb, gb, bbar, kb, b % tilesB, b / tilesB);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1177,11 +1198,6 @@ __global__ __launch_bounds__(256) void k_crt_c(const int8_t *__restrict__ planes
 // ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
-__global__ void k_fill_i32(int32_t *p, int64_t count, int32_t v) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < count) p[i] = v;
-}
-
 template <class T>
 __global__ void k_zero_c(T *C, int64_t m, int64_t n, int64_t ldc) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1270,9 +1286,11 @@ hipError_t launch_scale(Elem el, bool cplx, const void *A, int64_t m, int64_t k,
 }
 
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
-    OZ2_LAUNCH(ev, k_row_exponents, dim3(nblk(L.m_pad, 256)), dim3(256), 0, s, (const double *)(ws + L.part_s),
+    const int64_t span = L.m_pad > L.n_pad ? L.m_pad : L.n_pad;
+    OZ2_LAUNCH(ev, k_row_exponents, dim3(nblk(span, 256)), dim3(256), 0, s, (const double *)(ws + L.part_s),
                (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad), m, L.m_pad, L.nchunks, Pp,
-               (int32_t *)(ws + L.e), (int32_t *)(ws + L.ga));
+               (int32_t *)(ws + L.e), (int32_t *)(ws + L.ga), (int32_t *)(ws + L.rowmax),
+               (int32_t *)(ws + L.colmax), L.n_pad);
     return hipGetLastError();
 }
 
@@ -1306,28 +1324,21 @@ hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t ld
 }
 
 template <class T>
-static hipError_t launch_quantize_t(const T *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                                    const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L,
-                                    hipStream_t s) {
-    dim3 grid((unsigned)(rows_pad / kSplitRows), (unsigned)(L.k_pad / kSplitCols));
-    if (k_contiguous)
-        hipLaunchKernelGGL((k_quantize<true, T>), grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
-    else
-        hipLaunchKernelGGL((k_quantize<false, T>), grid, dim3(256), 0, s, X, rows, k, ld, gx, out, L.kb);
+static hipError_t launch_quantize_t(const T *A, int64_t m, int64_t lda, const T *B, int64_t n, int64_t ldb,
+                                    int64_t k, const Layout &L, char *ws, hipStream_t s) {
+    const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows, tilesK = L.k_pad / kSplitCols;
+    const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
+    hipLaunchKernelGGL(k_quantize<T>, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA,
+                       tilesB, nA, (const int32_t *)(ws + L.ga), (const int32_t *)(ws + L.gb), (int8_t *)(ws + L.abar),
+                       (int8_t *)(ws + L.bbar), L.kb);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize(Elem el, const void *X, int64_t rows, int64_t k, int64_t ld, bool k_contiguous,
-                           const int32_t *gx, int8_t *out, int64_t rows_pad, const Layout &L, hipStream_t s) {
+hipError_t launch_quantize(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
+                           int64_t k, const Layout &L, char *ws, hipStream_t s) {
     if (el == Elem::f32)
-        return launch_quantize_t((const float *)X, rows, k, ld, k_contiguous, gx, out, rows_pad, L, s);
-    return launch_quantize_t((const double *)X, rows, k, ld, k_contiguous, gx, out, rows_pad, L, s);
-}
-
-hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s) {
-    if (count <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_fill_i32, dim3(nblk(count, 256)), dim3(256), 0, s, p, count, value);
-    return hipGetLastError();
+        return launch_quantize_t((const float *)A, m, lda, (const float *)B, n, ldb, k, L, ws, s);
+    return launch_quantize_t((const double *)A, m, lda, (const double *)B, n, ldb, k, L, ws, s);
 }
 
 static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L) {

@@ -157,3 +157,46 @@ def test_zgemm_k_zero_and_ws_entry():
     c = dC.cpu().numpy()
     assert_bitwise_equal(c[:, :, 0].T.copy(), g["C_re"], "ws Re")
     assert_bitwise_equal(c[:, :, 1].T.copy(), g["C_im"], "ws Im")
+
+
+def test_zgemm_config_4096_n16():
+    # the complex workload at full size, in the benchmark's launch configuration
+    A, B = W.make("zgemm_spread1.0_4096_n16")
+    m, k = A.shape
+    n = B.shape[1]
+    N = 16
+    dA, dB = dev_complex(A, m, False), dev_complex(B, k, False)
+    dC = torch.empty((n, m, 2), dtype=torch.float64, device="cuda")
+    wb = oz.ozaki2_zgemm_workspace_size(m, n, k, N, debug=True)
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    e = torch.empty(m, dtype=torch.int32, device="cuda")
+    f = torch.empty(n, dtype=torch.int32, device="cuda")
+    st = oz.ozaki2_zgemm_debug(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, oz.FAST,
+                               ws.data_ptr(), wb, e.data_ptr(), f.data_ptr(), None, None, None, None, stream_handle())
+    assert st == 0
+    del ws
+    wb2 = oz.ozaki2_zgemm_workspace_size(m, n, k, N)
+    ws2 = torch.empty(wb2, dtype=torch.uint8, device="cuda")
+    dC2 = torch.empty((n, m, 2), dtype=torch.float64, device="cuda")
+    st = oz.ozaki2_zgemm_ws(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC2.data_ptr(), m, N, oz.FAST,
+                            ws2.data_ptr(), wb2, stream_handle())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(dC.view(torch.int64), dC2.view(torch.int64)), "ws vs debug"
+    del ws2, dC2
+    ge, gf = e.cpu().numpy().tolist(), f.cpu().numpy().tolist()
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(m, 12, replace=False)).tolist()
+    cols = np.sort(rng.choice(n, 12, replace=False)).tolist()
+    Pp = O.scaling_constant(math.prod(O.choose_moduli(N)))
+    oe = O.complex_exponents_rows(A.real[rows], A.imag[rows], Pp)
+    of = O.complex_exponents_rows(B.real[:, cols].T, B.imag[:, cols].T, Pp)
+    assert sum(a != b for a, b in zip(oe, [ge[i] for i in rows])) <= 1
+    assert sum(a != b for a, b in zip(of, [gf[j] for j in cols])) <= 1
+    er, fc = [ge[i] for i in rows], [gf[j] for j in cols]
+    Xr, Xi = O.exact_complex_scaled_product(A[rows], B[:, cols], er, fc)
+    Cs = dC[cols][:, rows].cpu().numpy()  # [col][row][part]
+    ref_r = O.unscale(Xr, er, fc)
+    ref_i = O.unscale(Xi, er, fc)
+    assert_bitwise_equal(np.ascontiguousarray(Cs[:, :, 0].T), ref_r, "sampled Re C")
+    assert_bitwise_equal(np.ascontiguousarray(Cs[:, :, 1].T), ref_i, "sampled Im C")
