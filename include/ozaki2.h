@@ -32,7 +32,8 @@
  *   mode      OZAKI2_FAST: the scale-invariant Cauchy-Schwarz scaling of [G]
  *             section Methodik; OZAKI2_ACCURATE: one extra INT8 GEMM bounds
  *             the products before scaling ([Q] section
- *             2の累乗による整数化(手順1と5), [G] section Problemstellung).
+ *             2の累乗による整数化(手順1と5), [G] section Problemstellung);
+ *             OZAKI2_FAST_ORIGINAL: comparison stand-in, see enum ozaki2_mode.
  *   stream    hipStream_t to enqueue on (NULL = default stream). All device
  *             work is asynchronous; no call synchronises the stream.
  *
@@ -63,8 +64,15 @@ extern "C" {
 #endif
 
 enum ozaki2_mode {
-    OZAKI2_FAST = 0,     /* proposed scale-invariant fast-mode scaling ([G] Methodik) */
-    OZAKI2_ACCURATE = 1  /* extra INT8 bound GEMM ([G] Problemstellung, mode 1) */
+    OZAKI2_FAST = 0,          /* proposed scale-invariant fast-mode scaling ([G] Methodik) */
+    OZAKI2_ACCURATE = 1,      /* extra INT8 bound GEMM ([G] Problemstellung, mode 1) */
+    OZAKI2_FAST_ORIGINAL = 2  /* for comparisons only: a stand-in for the original fast-mode rule that
+                                 [G] Problemstellung shows is not scale invariant (the pages do not
+                                 print it): squares of the binary32-rounded entries summed in binary32,
+                                 e = floor(P' - 0.5 log2f(sum)), no margin; an overflowed sum gives
+                                 mu = 0 and one that underflows to zero leaves mu unbounded, the two
+                                 failure directions [G] describes. Results are not guaranteed to
+                                 reconstruct; real operands only. */
 };
 
 enum ozaki2_status {

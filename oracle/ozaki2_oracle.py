@@ -42,6 +42,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   * log2 is applied only to the significand f in [1, 2) of that sum, and the
     binary exponent is split off exactly, so no rounding depends on it.
   * "cut off" is truncation toward zero.
+  * The original fast-mode rule [G] criticises is not printed; the stand-in
+    original_exponents_rows (binary32 sums, no margin) is for comparisons
+    only and PARITY UNPINNED beyond its stated failure directions.
   * Single precision ([G] section Zentrale Beiträge names SGEMM): the same
     steps on the binary32 inputs widened exactly to doubles, and one rounding
     of X * 2^-(e+f) to binary32 (os2_sgemm, round_to_f32).
@@ -265,6 +268,38 @@ def fast_exponents(A: np.ndarray, B: np.ndarray, Pp: float):
     return fast_exponents_rows(A, Pp), fast_exponents_rows(np.asarray(B).T, Pp)
 
 
+# Stand-in for the original fast-mode rule ([G] Problemstellung criticises it
+# but the pages do not print it; PARITY UNPINNED beyond its stated behaviour):
+# squares of the binary32-rounded entries summed in binary32 in ascending h,
+# e = floor(P' - 0.5 * log2(sum)) in binary32 with no margin and no exponent
+# split. A sum that overflows gives mu = 0 (EXP_COLLAPSE: every integer is 0);
+# a nonzero line whose sum underflows to zero leaves mu unbounded (EXP_FLOOD).
+EXP_COLLAPSE, EXP_FLOOD = -2000, 2000
+
+
+def original_exponents_rows(X: np.ndarray, Pp: float) -> list:
+    X = np.asarray(X, dtype=np.float64)
+    out = []
+    with np.errstate(over="ignore", under="ignore"):
+        for row in X:
+            if not np.all(np.isfinite(row)):
+                out.append(NONFINITE)
+                continue
+            a = row.astype(np.float32)
+            s = np.float32(0.0)
+            for v in a:
+                s = np.float32(s + np.float32(v * v))
+            if not np.any(row != 0.0):
+                out.append(0)
+            elif s == 0.0:
+                out.append(EXP_FLOOD)
+            elif not np.isfinite(s):
+                out.append(EXP_COLLAPSE)
+            else:
+                out.append(int(np.floor(np.float32(Pp) - np.float32(0.5) * np.log2(s))))
+    return out
+
+
 def accurate_bound_operands(A: np.ndarray, B: np.ndarray):
     """6-bit integer upper bounds of |A| and |B| (accurate mode, our reading).
 
@@ -450,6 +485,8 @@ def exponents(A, B, num_moduli: int, mode: str = "fast"):
     if mode == "accurate":
         e, f, _ = accurate_exponents(A, B, Pp)
         return e, f
+    if mode == "original":
+        return original_exponents_rows(A, Pp), original_exponents_rows(np.asarray(B).T, Pp)
     raise ValueError(mode)
 
 

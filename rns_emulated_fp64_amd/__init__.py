@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libozaki2.so")
 
 FAST = 0
 ACCURATE = 1
-MODES = {"fast": FAST, "accurate": ACCURATE}
+FAST_ORIGINAL = 2  # comparison stand-in for the original fast-mode rule (see include/ozaki2.h)
+MODES = {"fast": FAST, "accurate": ACCURATE, "original": FAST_ORIGINAL}
 PHASES = ("scale", "split", "gemm", "crt")
 
 #: every symbol include/ozaki2.h declares

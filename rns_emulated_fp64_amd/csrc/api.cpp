@@ -37,7 +37,7 @@ int validate(int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const 
     if (C == nullptr && m > 0 && n > 0) return -8;
     if (ldc < (m > 1 ? m : 1)) return -9;
     if (nmod < 2 || nmod > kMaxModuli) return -10;
-    if (mode != OZAKI2_FAST && mode != OZAKI2_ACCURATE) return -11;
+    if (mode != OZAKI2_FAST && mode != OZAKI2_ACCURATE && mode != OZAKI2_FAST_ORIGINAL) return -11;
     return 0;
 }
 
@@ -181,7 +181,9 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
     // Step 1: squared norms of the rows of A and exponents of the columns of
     // B ([G] Methodik), one launch.
     const int group = cplx ? 3 : 1;
-    HIP_TRY(launch_scale(el, cplx, A, m, k, lda, B, n, ldb, T->Pp, L, ws, s, ev_of(kPhaseScale, true, !accurate)));
+    const bool original = mode == OZAKI2_FAST_ORIGINAL;
+    HIP_TRY(launch_scale(el, cplx, original, A, m, k, lda, B, n, ldb, T->Pp, L, ws, s,
+                         ev_of(kPhaseScale, true, !accurate)));
     if (accurate) {
         // Accurate mode bounds the products with one extra INT8 GEMM first
         // ([G] Problemstellung).
@@ -194,7 +196,7 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
 
     // Steps 1 + 2: integerize and split both operands into residues, one
     // launch (in fast mode it also finishes the row exponents of A).
-    HIP_TRY(launch_split(el, cplx, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
+    HIP_TRY(launch_split(el, cplx, original, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
                          ev_of(kPhaseSplit, true, true)));
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
 

@@ -87,12 +87,14 @@ enum class Elem { f64, f32 };
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
 // cplx: interleaved complex operands (A, B, C hold (re, im) pairs; leading
 // dimensions count complex elements).
-hipError_t launch_scale(Elem el, bool cplx, const void *A, int64_t m, int64_t k, int64_t lda, const void *B,
-                        int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
+// original: the stand-in exponents of OZAKI2_FAST_ORIGINAL (real operands only).
+hipError_t launch_scale(Elem el, bool cplx, bool original, const void *A, int64_t m, int64_t k, int64_t lda,
+                        const void *B, int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s,
+                        Ev ev = {});
 hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
-hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t lda, const void *B, int64_t n,
-                        int64_t ldb, int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc,
-                        const Layout &L, char *ws, hipStream_t s, Ev ev = {});
+hipError_t launch_split(Elem el, bool cplx, bool original, const void *A, int64_t m, int64_t lda, const void *B,
+                        int64_t n, int64_t ldb, int64_t k, bool fold_row_exponents, double Pp,
+                        const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev = {});
 hipError_t launch_quantize(Elem el, const void *A, int64_t m, int64_t lda, const void *B, int64_t n, int64_t ldb,
                            int64_t k, const Layout &L, char *ws, hipStream_t s);
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int group, const ModConsts &mc,

@@ -80,12 +80,30 @@ __device__ __forceinline__ int exponent_from_bound(double s, double Pp) {
     return (int)floor(z) - h;
 }
 
+// The stand-in for the original fast-mode rule that [G] (Problemstellung)
+// shows is not scale invariant (OZAKI2_FAST_ORIGINAL; the pages do not print
+// it): the squares of the binary32-rounded entries are summed in binary32,
+// and e = floor(P' - 0.5 log2f(s)) with no margin and no exponent split.
+// An overflowed sum makes mu = 0 (kExpCollapse: every integer becomes 0); a
+// sum that underflows to zero on a nonzero line makes mu unbounded
+// (kExpFlood: the integers overflow the CRT range). Both are the failure
+// directions [G] describes; the result is not checked against anything.
+constexpr int kExpCollapse = -2000, kExpFlood = 2000;
+__device__ __forceinline__ int exponent_original(float s, bool nonzero, double Pp) {
+    if (!nonzero) return 0;
+    if (s == 0.0f) return kExpFlood;
+    if (!(s <= FLT_MAX)) return kExpCollapse;
+    return (int)floorf((float)Pp - 0.5f * log2f(s));
+}
+
 // Rows of column-major A. Block = 64 rows x 4 k-lanes over one k-chunk: a
 // wavefront reads 64 consecutive rows of one column (512 contiguous bytes),
 // each thread accumulates every 4th column of its chunk, and the 4 lanes of a
 // row are merged in a fixed order through LDS. Output: one partial
 // (s, g, nonfinite) per (chunk, row).
-template <class T, int W>
+// ORIG: the stand-in's binary32 sum; the partial holds that float (as a
+// double) and pg holds 1 if the chunk has a nonzero entry.
+template <class T, int W, bool ORIG = false>
 __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                 int64_t kchunk, double *__restrict__ ps, int *__restrict__ pg,
                                                 int *__restrict__ pbad, int64_t rowblock, int64_t chunk) {
@@ -99,6 +117,19 @@ __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t
     double s = 0.0;
     int g = kExpEmpty;
     int bad = 0;
+    float s32 = 0.0f;
+    auto add = [&](double x) {  // x = |entry|
+        if (!(x <= DBL_MAX)) {
+            bad = 1;
+        } else if (ORIG) {
+            const float a = (float)x;
+            s32 = s32 + a * a;
+            g |= x != 0.0 ? 1 : 0;
+        } else {
+            ssq_add(s, g, x);
+        }
+    };
+    if (ORIG) g = 0;
     if (i < m) {
         // element (i, h) part c at A[(i + h*lda)*W + c]
         const T *a = A + i * W;
@@ -113,20 +144,13 @@ __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int c = 0; c < W; ++c) {
-                    double x = fabs(v[u][c]);
-                    if (!(x <= DBL_MAX)) bad = 1;
-                    else ssq_add(s, g, x);
-                }
+                for (int c = 0; c < W; ++c) add(fabs(v[u][c]));
         }
         for (; h < h1; h += 4)
 #pragma unroll
-            for (int c = 0; c < W; ++c) {
-                double x = fabs((double)a[h * cs + c]);
-                if (!(x <= DBL_MAX)) bad = 1;
-                else ssq_add(s, g, x);
-            }
+            for (int c = 0; c < W; ++c) add(fabs((double)a[h * cs + c]));
     }
+    if (ORIG) s = (double)s32;
     sh_s[kl][r] = s;
     sh_g[kl][r] = g;
     sh_b[kl][r] = bad;
@@ -134,9 +158,15 @@ __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t
     if (kl == 0 && i < m) {
 #pragma unroll
         for (int q = 1; q < 4; ++q) {
-            ssq_merge(s, g, sh_s[q][r], sh_g[q][r]);
+            if (ORIG) {
+                s32 = s32 + (float)sh_s[q][r];
+                g |= sh_g[q][r];
+            } else {
+                ssq_merge(s, g, sh_s[q][r], sh_g[q][r]);
+            }
             bad |= sh_b[q][r];
         }
+        if (ORIG) s = (double)s32;
         const int64_t o = chunk * m + i;
         ps[o] = s;
         pg[o] = g;
@@ -146,6 +176,7 @@ __device__ __forceinline__ void row_norms_block(const T *__restrict__ A, int64_t
 
 // Exponent of row i from its chunk partials, merged in ascending chunk order:
 // e = fast exponent, g = max exponent (the r_i of accurate mode).
+template <bool ORIG = false>
 __device__ __forceinline__ void row_exponent_from_partials(const double *__restrict__ ps,
                                                            const int *__restrict__ pg,
                                                            const int *__restrict__ pbad, int64_t m, int64_t i,
@@ -153,6 +184,8 @@ __device__ __forceinline__ void row_exponent_from_partials(const double *__restr
     double s = 0.0;
     int g = kExpEmpty;
     int bad = 0;
+    float s32 = 0.0f;
+    int nonzero = 0;
     // loads in batches of 8 (all issued before the merges), merges in
     // ascending chunk order
     for (int c0 = 0; c0 < nchunks; c0 += 8) {
@@ -169,9 +202,19 @@ __device__ __forceinline__ void row_exponent_from_partials(const double *__restr
         for (int u = 0; u < 8; ++u) {
             if (c0 + u < nchunks) {
                 bad |= vb[u];
-                ssq_merge(s, g, vs[u], vg[u]);
+                if (ORIG) {
+                    s32 = s32 + (float)vs[u];
+                    nonzero |= vg[u];
+                } else {
+                    ssq_merge(s, g, vs[u], vg[u]);
+                }
             }
         }
+    }
+    if (ORIG) {
+        e = bad ? kExpNonfinite : exponent_original(s32, nonzero != 0, Pp);
+        g_out = 0;
+        return;
     }
     if (bad) {
         e = kExpNonfinite;
@@ -206,7 +249,7 @@ __global__ __launch_bounds__(256) void k_row_exponents(const double *__restrict_
 // Columns of column-major B (contiguous): one wavefront per column, lanes
 // stride the column, then a fixed xor-butterfly merge (every lane ends with
 // the same bits).
-template <class T>
+template <class T, bool ORIG = false>
 __device__ __forceinline__ void col_exponents_block(const T *__restrict__ B, int64_t k, int64_t n,
                                                     int64_t n_pad, int64_t ldb, double Pp, int32_t *__restrict__ f,
                                                     int32_t *__restrict__ gb, int64_t blk) {
@@ -224,31 +267,48 @@ __device__ __forceinline__ void col_exponents_block(const T *__restrict__ B, int
     double s = 0.0;
     int g = kExpEmpty;
     int bad = 0;
+    float s32 = 0.0f;
+    if (ORIG) g = 0;
+    auto add = [&](double x) {  // x = |entry|
+        if (!(x <= DBL_MAX)) {
+            bad = 1;
+        } else if (ORIG) {
+            const float a = (float)x;
+            s32 = s32 + a * a;
+            g |= x != 0.0 ? 1 : 0;
+        } else {
+            ssq_add(s, g, x);
+        }
+    };
     int64_t h = lane;
     for (; h + 7 * 64 < k; h += 8 * 64) {
         double v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = (double)col[h + 64 * u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            double x = fabs(v[u]);
-            if (!(x <= DBL_MAX)) bad = 1;
-            else ssq_add(s, g, x);
-        }
+        for (int u = 0; u < 8; ++u) add(fabs(v[u]));
     }
-    for (; h < k; h += 64) {
-        double x = fabs((double)col[h]);
-        if (!(x <= DBL_MAX)) bad = 1;
-        else ssq_add(s, g, x);
-    }
+    for (; h < k; h += 64) add(fabs((double)col[h]));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-        double s2 = __shfl_xor(s, off, 64);
-        int g2 = __shfl_xor(g, off, 64);
         bad |= __shfl_xor(bad, off, 64);
-        // the merge is symmetric in its two operands, so both lanes of a pair
-        // end with the same bits
-        ssq_merge(s, g, s2, g2);
+        if (ORIG) {
+            s32 = s32 + __shfl_xor(s32, off, 64);  // a + b == b + a: both lanes agree
+            g |= __shfl_xor(g, off, 64);
+        } else {
+            double s2 = __shfl_xor(s, off, 64);
+            int g2 = __shfl_xor(g, off, 64);
+            // the merge is symmetric in its two operands, so both lanes of a
+            // pair end with the same bits
+            ssq_merge(s, g, s2, g2);
+        }
+    }
+    if (ORIG) {
+        if (lane == 0) {
+            f[j] = bad ? kExpNonfinite : exponent_original(s32, g != 0, Pp);
+            gb[j] = 0;
+        }
+        return;
     }
     if (lane == 0) {
         if (bad) {
@@ -268,7 +328,7 @@ __device__ __forceinline__ void col_exponents_block(const T *__restrict__ B, int
 // of A (row block fastest, then k-chunk), the rest column blocks of B. W = 2:
 // complex operands with interleaved parts; a row's (column's) squared norm is
 // the sum over both parts, and a column of B is then 2k contiguous values.
-template <class T, int W>
+template <class T, int W, bool ORIG>
 __global__ __launch_bounds__(256) void k_scale(const T *__restrict__ A, int64_t m, int64_t k, int64_t lda,
                                                int64_t kchunk, int64_t rowblocks, int64_t nA,
                                                double *__restrict__ ps, int *__restrict__ pg,
@@ -277,9 +337,9 @@ __global__ __launch_bounds__(256) void k_scale(const T *__restrict__ A, int64_t 
                                                int32_t *__restrict__ gb) {
     const int64_t bid = blockIdx.x;
     if (bid < nA)
-        row_norms_block<T, W>(A, m, k, lda, kchunk, ps, pg, pbad, bid % rowblocks, bid / rowblocks);
+        row_norms_block<T, W, ORIG>(A, m, k, lda, kchunk, ps, pg, pbad, bid % rowblocks, bid / rowblocks);
     else
-        col_exponents_block(B, k * W, n, n_pad, ldb * W, Pp, f, gb, bid - nA);
+        col_exponents_block<T, ORIG>(B, k * W, n, n_pad, ldb * W, Pp, f, gb, bid - nA);
 }
 
 // Accurate mode: e_i = floor(P' + 6 - r_i - 0.5 (log2 R_i + 4 u32)) with R_i
@@ -506,7 +566,7 @@ __device__ __forceinline__ void split_block_c(const T *__restrict__ X, int64_t r
 // exponents of A's rows are merged here from the row-norm partials (the first
 // K tile of each row tile also stores them for the reconstruction); otherwise
 // they are read from e.
-template <bool FOLD, class T, int W>
+template <bool FOLD, class T, int W, bool ORIG>
 __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t m, int64_t lda,
                                                const T *__restrict__ B, int64_t n, int64_t ldb, int64_t kdim,
                                                int64_t tilesA, int64_t tilesB, int64_t nA,
@@ -533,7 +593,7 @@ __global__ __launch_bounds__(256) void k_split(const T *__restrict__ A, int64_t 
             if (threadIdx.x < kSplitRows) {
                 const int64_t i = bx * kSplitRows + threadIdx.x;
                 int ev = 0, gv = 0;
-                if (i < m) row_exponent_from_partials(ps, pg, pbad, m, i, nchunks, Pp, ev, gv);
+                if (i < m) row_exponent_from_partials<ORIG>(ps, pg, pbad, m, i, nchunks, Pp, ev, gv);
                 sh_e[threadIdx.x] = ev;
                 if (by == 0) e[i] = ev;  // i < m_pad: the workspace holds m_pad entries
             }
@@ -1261,26 +1321,29 @@ __global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t 
 static inline unsigned nblk(int64_t count, int per) { return (unsigned)((count + per - 1) / per); }
 static inline unsigned ydim(int64_t count) { return (unsigned)(count < 65535 ? (count > 0 ? count : 1) : 65535); }
 
-template <class T, int W>
+template <class T, int W, bool ORIG = false>
 static hipError_t launch_scale_t(const T *A, int64_t m, int64_t k, int64_t lda, const T *B, int64_t n, int64_t ldb,
                                  double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t rowblocks = (m + 63) / 64;
     const int64_t nA = rowblocks * L.nchunks, nB = L.n_pad / 4;
-    auto kern = k_scale<T, W>;
+    auto kern = k_scale<T, W, ORIG>;
     OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, k, lda, L.kchunk, rowblocks, nA,
                (double *)(ws + L.part_s), (int *)(ws + L.part_g), (int *)(ws + L.part_bad), B, n, L.n_pad, ldb, Pp,
                (int32_t *)(ws + L.f), (int32_t *)(ws + L.gb));
     return hipGetLastError();
 }
 
-hipError_t launch_scale(Elem el, bool cplx, const void *A, int64_t m, int64_t k, int64_t lda, const void *B,
-                        int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s, Ev ev) {
+hipError_t launch_scale(Elem el, bool cplx, bool original, const void *A, int64_t m, int64_t k, int64_t lda,
+                        const void *B, int64_t n, int64_t ldb, double Pp, const Layout &L, char *ws, hipStream_t s,
+                        Ev ev) {
     if (el == Elem::f32) {
         const float *a = (const float *)A, *b = (const float *)B;
+        if (original) return launch_scale_t<float, 1, true>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
         return cplx ? launch_scale_t<float, 2>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev)
                     : launch_scale_t<float, 1>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
     }
     const double *a = (const double *)A, *b = (const double *)B;
+    if (original) return launch_scale_t<double, 1, true>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
     return cplx ? launch_scale_t<double, 2>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev)
                 : launch_scale_t<double, 1>(a, m, k, lda, b, n, ldb, Pp, L, ws, s, ev);
 }
@@ -1294,13 +1357,13 @@ hipError_t launch_row_exponents(int64_t m, double Pp, const Layout &L, char *ws,
     return hipGetLastError();
 }
 
-template <bool FOLD, class T, int W>
+template <bool FOLD, class T, int W, bool ORIG = false>
 static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B, int64_t n, int64_t ldb, int64_t k,
                                  double Pp, const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     const int64_t tilesA = L.m_pad / kSplitRows, tilesB = L.n_pad / kSplitRows;
     const int64_t tilesK = L.k_pad / (W == 2 ? kSplitColsC : kSplitCols);
     const int64_t nA = tilesA * tilesK, nB = tilesB * tilesK;
-    auto kern = k_split<FOLD, T, W>;
+    auto kern = k_split<FOLD, T, W, ORIG>;
     OZ2_LAUNCH(ev, kern, dim3((unsigned)(nA + nB)), dim3(256), 0, s, A, m, lda, B, n, ldb, k, tilesA, tilesB, nA,
                (const double *)(ws + L.part_s), (const int *)(ws + L.part_g), (const int *)(ws + L.part_bad),
                L.nchunks, Pp, (int32_t *)(ws + L.e), (const int32_t *)(ws + L.f), sc, (int8_t *)(ws + L.ra),
@@ -1308,16 +1371,18 @@ static hipError_t launch_split_t(const T *A, int64_t m, int64_t lda, const T *B,
     return hipGetLastError();
 }
 
-hipError_t launch_split(Elem el, bool cplx, const void *A, int64_t m, int64_t lda, const void *B, int64_t n,
-                        int64_t ldb, int64_t k, bool fold_row_exponents, double Pp, const SplitConsts &sc,
-                        const Layout &L, char *ws, hipStream_t s, Ev ev) {
+hipError_t launch_split(Elem el, bool cplx, bool original, const void *A, int64_t m, int64_t lda, const void *B,
+                        int64_t n, int64_t ldb, int64_t k, bool fold_row_exponents, double Pp,
+                        const SplitConsts &sc, const Layout &L, char *ws, hipStream_t s, Ev ev) {
     if (el == Elem::f32) {
         const float *a = (const float *)A, *b = (const float *)B;
+        if (original) return launch_split_t<true, float, 1, true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
         if (cplx) return launch_split_t<true, float, 2>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
         return fold_row_exponents ? launch_split_t<true, float, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
                                   : launch_split_t<false, float, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
     }
     const double *a = (const double *)A, *b = (const double *)B;
+    if (original) return launch_split_t<true, double, 1, true>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
     if (cplx) return launch_split_t<true, double, 2>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);
     return fold_row_exponents ? launch_split_t<true, double, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev)
                               : launch_split_t<false, double, 1>(a, m, lda, b, n, ldb, k, Pp, sc, L, ws, s, ev);

@@ -74,7 +74,7 @@ P = 1 << 20  # a fake non-null pointer: validation fails before it is ever used
         ((4, 4, 4, P, 4, P, 4, P, 3, 8, 0), -9),
         ((4, 4, 4, P, 4, P, 4, P, 4, 1, 0), -10),
         ((4, 4, 4, P, 4, P, 4, P, 4, 21, 0), -10),
-        ((4, 4, 4, P, 4, P, 4, P, 4, 8, 2), -11),
+        ((4, 4, 4, P, 4, P, 4, P, 4, 8, 3), -11),
         ((4, 4, 4, P, 4, P, 4, P, 4, 8, -1), -11),
         ((4, 4, 1 << 22, P, 4, P, 1 << 22, P, 4, 8, 0), 3),
         ((4, 4, 1 << 19, P, 4, P, 1 << 19, P, 4, 8, 1), 3),
@@ -97,6 +97,7 @@ def test_complex_status_codes():
         assert fn(4, 4, 4, P, 3, P, 4, P, 4, 8, 0, 0) == -5
         assert fn(4, 4, 4, P, 4, P, 4, P, 4, 21, 0, 0) == -10
         assert fn(4, 4, 4, P, 4, P, 4, P, 4, 8, 1, 0) == 3
+        assert fn(4, 4, 4, P, 4, P, 4, P, 4, 8, 2, 0) == 3
         assert fn(0, 4, 4, 0, 1, P, 4, 0, 1, 8, 0, 0) == 0
     assert oz.ozaki2_zgemm_ws(4, 4, 4, P, 4, P, 4, P, 4, 8, 0, 0, 0, 0) == -12
     need = oz.ozaki2_zgemm_workspace_size(64, 64, 64, 8)

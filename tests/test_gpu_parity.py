@@ -226,6 +226,30 @@ def test_config_scale_sweep_2048_n14():
         _sampled_exact_check(A, B, base["C"], base["e"].tolist(), base["f"].tolist(), rows, cols)
 
 
+def test_scale_sweep_original_rule_stand_in():
+    # The comparison stand-in for the original fast-mode rule ([G] Problemstellung;
+    # not printed on the pages): its GPU exponents follow the oracle's binary32
+    # rule (summation order may move a few by one), it collapses at alpha = 2^64
+    # and is not scale invariant, while the proposed rule is. Logged, not gated
+    # on accuracy.
+    ones, ua, B = W.scale_sweep_case(2048)
+    Pp = O.scaling_constant(math.prod(O.choose_moduli(14)))
+    for A in (ones, ua):
+        prev = None
+        for s in (-64, -32, 0, 32, 64):
+            As = np.ldexp(A, s)
+            g = run_debug(As, B, 14, "original", want_prod=False, want_res=False)
+            oe = O.original_exponents_rows(As, Pp)
+            ge = g["e"].tolist()
+            diff = [a - b for a, b in zip(ge, oe)]
+            assert all(abs(d) <= 1 for d in diff) and sum(d != 0 for d in diff) <= 20, s
+            if s == 64:
+                assert all(v == O.EXP_COLLAPSE for v in ge) and np.all(g["C"] == 0.0)
+            print(f"original rule, {'ones' if A is ones else 'U'}, alpha=2^{s}: e[0]={ge[0]}, "
+                  f"C[0,0]={g['C'][0, 0]!r}")
+            prev = ge
+
+
 def test_config_spread1_16384_n18():
     # 16384^3, N = 18 (2 GiB per operand; |x| reaches 2^69.7, beyond int64):
     # exponents of sampled rows/columns, C bit-exact on sampled entries, and the

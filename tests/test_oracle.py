@@ -543,3 +543,28 @@ def test_complex_accuracy_against_native():
     assert ecw(O.os2_zgemm(A, B, 16)["C"]) <= 1e-15
     assert ecw(O.os2_zgemm(A, B, 8, single=True)["C"].astype(np.complex128)) <= \
         ecw((A.astype(np.complex64) @ B.astype(np.complex64)).astype(np.complex128))
+
+
+# --------------------------------------------------------------------------
+# The stand-in for the original fast-mode rule ([G] Problemstellung): pinned
+# only by the behaviour [G] describes, not by values
+# --------------------------------------------------------------------------
+def test_original_rule_lacks_scale_invariance_and_fails_at_the_ends():
+    Pp = O.scaling_constant(math.prod(O.choose_moduli(14)))
+    rng = np.random.default_rng(4)
+    U = rng.uniform(-1.0, 1.0, (6, 2048))
+    base = O.original_exponents_rows(U, Pp)
+    prop = O.fast_exponents_rows(U, Pp)
+    # at moderate scale it picks about the proposed exponent (no margin: at most one more)
+    assert all(0 <= b - p <= 1 for b, p in zip(base, prop))
+    # large alpha: the binary32 sum overflows and the bit width collapses (mu = 0)
+    big = O.original_exponents_rows(np.ldexp(U, 64), Pp)
+    assert big == [O.EXP_COLLAPSE] * 6
+    # tiny alpha: the binary32 squares underflow and mu is unbounded
+    tiny = O.original_exponents_rows(np.ldexp(U, -90), Pp)
+    assert tiny == [O.EXP_FLOOD] * 6
+    # the proposed rule is exact over the same range
+    for s in (64, -66, -90):
+        assert O.fast_exponents_rows(np.ldexp(U, s), Pp) == [p - s for p in prop]
+    # zero rows stay zero in both
+    assert O.original_exponents_rows(np.zeros((2, 9)), Pp) == [0, 0]
