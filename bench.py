@@ -30,7 +30,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="spread1.0_4096_n16")
-    p.add_argument("--mode", default="fast", choices=["fast", "accurate"])
+    p.add_argument("--mode", default="fast", choices=["fast", "accurate", "original"],
+                   help="original: the comparison stand-in for the original fast-mode rule")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the accurate-mode and native-FP64 context runs")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of A in the oracle sample (0: automatic)")
@@ -300,7 +301,7 @@ def main():
         del Azt, Bzt
     elif not args.no_extras:
         # accurate mode (the other mode) and native FP64 on the same operands, as context
-        other = "accurate" if args.mode == "fast" else "fast"
+        other = "accurate" if args.mode != "accurate" else "fast"
         w2, wb2 = workspace(oz.MODES[other])
         ms2 = time_steps(lambda: step(oz.MODES[other], w2, wb2), max(args.steps // 2, 3), 2, torch)
         extras[f"{other}_mode_tflops"] = round(flops / (ms2 * 1e-3) / 1e12, 3)

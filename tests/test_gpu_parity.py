@@ -157,6 +157,10 @@ def test_config_spread05_1024_n14():
     native = O.error_metrics(A @ B, hi, lo, A, B)
     print("1024^3 N=14:", err, "native:", native, "exponent mismatches:", mism)
     assert err["E_cw"] <= 1e-14
+    # proposed vs the stand-in for the original rule on the same operands (logged)
+    go = run_debug(A, B, 14, "original", want_prod=False, want_res=False)
+    erro = O.error_metrics(go["C"], hi, lo, A, B)
+    print("1024^3 N=14 original-rule stand-in:", erro)
 
 
 def _sampled_exact_check(A, B, C, e, f, rows, cols):
