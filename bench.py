@@ -32,6 +32,7 @@ def parse():
     p.add_argument("--config", default="spread1.0_4096_n16")
     p.add_argument("--mode", default="fast", choices=["fast", "accurate", "original"],
                    help="original: the comparison stand-in for the original fast-mode rule")
+    p.add_argument("--num-moduli", type=int, default=0, help="override the workload's number of moduli")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="skip the accurate-mode and native-FP64 context runs")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of A in the oracle sample (0: automatic)")
@@ -230,6 +231,7 @@ def main():
     if cfg["kind"] == "sweep":
         return sweep_main(args, cfg, torch, oz, W, np)
     m, n, k, N = cfg["m"], cfg["n"], cfg["k"], cfg["num_moduli"]
+    N = args.num_moduli or N
     single = bool(cfg.get("single"))
     cplx = bool(cfg.get("complex"))
     md = oz.MODES[args.mode]

@@ -730,6 +730,30 @@ __device__ __forceinline__ int smod(int q, double p, double pinv) {
     return (int)fma(-p, rint(y * pinv), y);
 }
 
+// Step 3 output of one wavefront: its 4 x 4 accumulator tiles reduced mod p
+// and stored with 16-byte stores. A lane's four packed words hold rows
+// {0-3, 8-11, 16-19, 24-27} (lanes 0-31) or {4-7, 12-15, 20-23, 28-31}
+// (lanes 32-63) of its column; lanes L and L + 32 trade two words so that
+// each ends up with 16 consecutive rows.
+__device__ __forceinline__ void store_mod_tiles(const v16i (&acc)[4][4], double p, double pinv, int8_t *plane,
+                                                int64_t m_pad, int row0, int col_base, int lane) {
+    const bool hi = lane >= 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                w[g] = pack4(smod(acc[i][j][4 * g + 0], p, pinv), smod(acc[i][j][4 * g + 1], p, pinv),
+                             smod(acc[i][j][4 * g + 2], p, pinv), smod(acc[i][j][4 * g + 3], p, pinv));
+            const uint32_t r1 = __shfl_xor(hi ? w[0] : w[2], 32, 64);
+            const uint32_t r2 = __shfl_xor(hi ? w[1] : w[3], 32, 64);
+            const uint4 o = hi ? make_uint4(r1, w[2], r2, w[3]) : make_uint4(w[0], r1, w[1], r2);
+            *(uint4 *)(plane + (int64_t)(col_base + 32 * j) * m_pad + row0 + 32 * i + (hi ? 16 : 0)) = o;
+        }
+}
+
 // KBLK: the inner dimension spans more than kReduceStages stages and the
 // accumulators are folded between blocks (a separate instance, so that the
 // common case carries no fold code and no register spills).
@@ -851,21 +875,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int row_base = tm * kTileM + wm * 128 + 4 * (lane >> 5);
     const int col_base = tn * kTileN + wn * 128 + (lane & 31);
     if (EPI == EPI_MOD) {
-        const double p = mc.p[l / ga.group], pinv = mc.pinv[l / ga.group];
-        int8_t *plane = ga.planes + (int64_t)l * ga.plane_elems;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = col_base + 32 * j;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int row = row_base + 32 * i + 8 * g;
-                    uint32_t w = pack4(smod(acc[i][j][4 * g + 0], p, pinv), smod(acc[i][j][4 * g + 1], p, pinv),
-                                       smod(acc[i][j][4 * g + 2], p, pinv), smod(acc[i][j][4 * g + 3], p, pinv));
-                    *(uint32_t *)(plane + col * ga.m_pad + row) = w;
-                }
-            }
+        store_mod_tiles(acc, mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
+                        ga.m_pad, tm * kTileM + wm * 128, col_base, lane);
     } else if (EPI == EPI_RAW) {
         int32_t *plane = ga.raw + (int64_t)l * ga.plane_elems;
 #pragma unroll
