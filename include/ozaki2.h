@@ -88,7 +88,7 @@ enum ozaki2_status {
 /* Inner dimension limits. int32 sums of int8 x int8 products are exact only
  * below 2^17 terms ([Q] section 誤差のないINT8行列積(手順3)); longer inner
  * dimensions are handled in blocks (the GEMM reduces its accumulators mod p
- * every 2047 * 64 terms). The accurate-mode bound product (entries <= 64 * 64
+ * every 1024 * 64 terms). The accurate-mode bound product (entries <= 64 * 64
  * per term) stays exact below 2^19 terms. */
 #define OZAKI2_MAX_K ((1 << 22) - 1)
 #define OZAKI2_MAX_K_ACCURATE ((1 << 19) - 1)

@@ -679,7 +679,7 @@ constexpr int kFB = (kTileN / 32) * kKS;   // B fragment blocks per stage (16)
 constexpr int kStageBytes = (kFA + kFB) * 1024;
 constexpr int kLoadsPerWave = (kFA + kFB) / 4;
 constexpr int kGroupM = 4;                 // tile rows per raster group
-constexpr int kReduceStages = 2047;        // 2047 * 64 * 2^14 + 128 < 2^31
+constexpr int kReduceStages = 1024;        // 1024 * 64 * 2^14 = 2^30: the range of smod
 static_assert(kKS == 2, "the main loop is written for two substeps per stage");
 // DMA copies a wave may leave in flight at a stage barrier: kNST-2 stages
 #define OZ2_GEMM_VMCNT "16"
@@ -721,13 +721,17 @@ __device__ __forceinline__ void decode_block(int bid, int total, int tiles_m, in
     tn = in / gsz;
 }
 
-// Symmetric residue of an exact int32 product modulo p: |q| < 2^31, so
-// rint(q/p) is the nearest integer for odd p >= 173 (no ties) and exact for
-// p = 256; r lies in [-(p-1)/2, (p-1)/2] (or [-128, 128], stored as a byte,
-// where 128 and -128 are the same residue).
-__device__ __forceinline__ int smod(int q, double p, double pinv) {
-    const double y = (double)q;
-    return (int)fma(-p, rint(y * pinv), y);
+// Symmetric residue r = q - p * round(q / p) of an int32 sum with
+// |q| <= 2^30 + 128. One FMA, t = RN(q * RN(1/p) + 1.5 * 2^52), leaves
+// round(q / p) in the low word of t: the product is off from q / p by less
+// than 2^-30, while for odd p >= 173 q / p is never closer than 1/(2p) to a
+// half-integer; for p = 256 the product is exact and the FMA rounds ties to
+// even. |round(q / p)| < 2^23, so q - k p is exact with the 24-bit multiplier.
+// r lies in [-(p-1)/2, (p-1)/2] (or [-128, 128] for p = 256, stored as a
+// byte, where 128 and -128 are the same residue).
+__device__ __forceinline__ int smod(int q, double pinv, int p) {
+    const double t = fma((double)q, pinv, 0x1.8p52);
+    return q - __mul24(__double2loint(t), p);
 }
 
 // Step 3 output of one wavefront: its 4 x 4 accumulator tiles reduced mod p
@@ -735,7 +739,7 @@ __device__ __forceinline__ int smod(int q, double p, double pinv) {
 // {0-3, 8-11, 16-19, 24-27} (lanes 0-31) or {4-7, 12-15, 20-23, 28-31}
 // (lanes 32-63) of its column; lanes L and L + 32 trade two words so that
 // each ends up with 16 consecutive rows.
-__device__ __forceinline__ void store_mod_tiles(const v16i (&acc)[4][4], double p, double pinv, int8_t *plane,
+__device__ __forceinline__ void store_mod_tiles(const v16i (&acc)[4][4], int p, double pinv, int8_t *plane,
                                                 int64_t m_pad, int row0, int col_base, int lane) {
     const bool hi = lane >= 32;
 #pragma unroll
@@ -745,8 +749,8 @@ __device__ __forceinline__ void store_mod_tiles(const v16i (&acc)[4][4], double 
             uint32_t w[4];
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                w[g] = pack4(smod(acc[i][j][4 * g + 0], p, pinv), smod(acc[i][j][4 * g + 1], p, pinv),
-                             smod(acc[i][j][4 * g + 2], p, pinv), smod(acc[i][j][4 * g + 3], p, pinv));
+                w[g] = pack4(smod(acc[i][j][4 * g + 0], pinv, p), smod(acc[i][j][4 * g + 1], pinv, p),
+                             smod(acc[i][j][4 * g + 2], pinv, p), smod(acc[i][j][4 * g + 3], pinv, p));
             const uint32_t r1 = __shfl_xor(hi ? w[0] : w[2], 32, 64);
             const uint32_t r2 = __shfl_xor(hi ? w[1] : w[3], 32, 64);
             const uint4 o = hi ? make_uint4(r1, w[2], r2, w[3]) : make_uint4(w[0], r1, w[1], r2);
@@ -855,16 +859,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         }
         if (KBLK && EPI == EPI_MOD && ks_end < nk) {
-            // Inner dimension in blocks ([Q] step 3): after 2047 stages
-            // (131008 terms of at most 2^14) fold the sums back to their
-            // symmetric residues, so they never leave int32.
-            const double p = mc.p[l / ga.group], pinv = mc.pinv[l / ga.group];
+            // Inner dimension in blocks ([Q] step 3): after 1024 stages
+            // (65536 terms of at most 2^14) fold the sums back to their
+            // symmetric residues, so they stay within smod's range.
+            const int p = (int)mc.p[l / ga.group];
+            const double pinv = mc.pinv[l / ga.group];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = smod(acc[i][j][v], p, pinv);
+                    for (int v = 0; v < 16; ++v) acc[i][j][v] = smod(acc[i][j][v], pinv, p);
                 }
         }
     }
@@ -875,7 +880,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int row_base = tm * kTileM + wm * 128 + 4 * (lane >> 5);
     const int col_base = tn * kTileN + wn * 128 + (lane & 31);
     if (EPI == EPI_MOD) {
-        store_mod_tiles(acc, mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
+        store_mod_tiles(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
                         ga.m_pad, tm * kTileM + wm * 128, col_base, lane);
     } else if (EPI == EPI_RAW) {
         int32_t *plane = ga.raw + (int64_t)l * ga.plane_elems;
