@@ -228,37 +228,68 @@ def dgemm(A, B, num_moduli: int = 16, mode="fast", out=None, workspace=None):
 
     Row-major C = A B is column-major C^T = B^T A^T, so the library is called
     with the operands swapped; the scaling is symmetric in the two operands.
+    ``out`` (optional) must be a contiguous (m, n) tensor of the same dtype on
+    the same device; ``workspace`` (optional) a device tensor of at least
+    ``ozaki2_workspace_size`` bytes.
     """
-    return _gemm(A, B, num_moduli, mode, out, workspace, single=False)
+    return _gemm(A, B, num_moduli, mode, out, workspace, "d")
 
 
 def sgemm(A, B, num_moduli: int = 8, mode="fast", out=None, workspace=None):
     """C = A @ B for float32 CUDA (HIP) tensors (ozaki2_sgemm), as dgemm."""
-    return _gemm(A, B, num_moduli, mode, out, workspace, single=True)
+    return _gemm(A, B, num_moduli, mode, out, workspace, "s")
 
 
-def _gemm(A, B, num_moduli, mode, out, workspace, single):
+def zgemm(A, B, num_moduli: int = 16, mode="fast", out=None, workspace=None):
+    """C = A @ B for complex128 CUDA (HIP) tensors (ozaki2_zgemm, fast mode), as
+    dgemm; a complex tensor's storage is the interleaved (re, im) layout the
+    library takes. ``workspace`` needs ``ozaki2_zgemm_workspace_size`` bytes."""
+    return _gemm(A, B, num_moduli, mode, out, workspace, "z")
+
+
+def cgemm(A, B, num_moduli: int = 16, mode="fast", out=None, workspace=None):
+    """C = A @ B for complex64 CUDA (HIP) tensors (ozaki2_cgemm), as zgemm."""
+    return _gemm(A, B, num_moduli, mode, out, workspace, "c")
+
+
+_KINDS = {  # dtype name, plain entry, workspace entry
+    "d": ("float64", "ozaki2_dgemm"),
+    "s": ("float32", "ozaki2_sgemm"),
+    "z": ("complex128", "ozaki2_zgemm"),
+    "c": ("complex64", "ozaki2_cgemm"),
+}
+
+
+def _gemm(A, B, num_moduli, mode, out, workspace, kind):
     import torch
 
-    dt = torch.float32 if single else torch.float64
-    if A.dtype != dt or B.dtype != dt or not A.is_cuda or not B.is_cuda:
-        raise TypeError(f"A and B must be {dt} tensors on the GPU")
+    dname, entry = _KINDS[kind]
+    dt = getattr(torch, dname)
+    if A.dtype != dt or B.dtype != dt or not A.is_cuda or not B.is_cuda or A.device != B.device:
+        raise TypeError(f"A and B must be {dt} tensors on the same GPU")
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError("shapes do not multiply")
     A = A.contiguous()
     B = B.contiguous()
     m, k = A.shape
     n = B.shape[1]
-    C = out if out is not None else torch.empty((m, n), dtype=dt, device=A.device)
+    if out is None:
+        C = torch.empty((m, n), dtype=dt, device=A.device)
+    else:
+        if out.dtype != dt or out.device != A.device or tuple(out.shape) != (m, n) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous ({m}, {n}) {dt} tensor on {A.device}")
+        C = out
     stream = torch.cuda.current_stream(A.device).cuda_stream
     md = _mode(mode)
-    plain, ws_form = (ozaki2_sgemm, ozaki2_sgemm_ws) if single else (ozaki2_dgemm, ozaki2_dgemm_ws)
+    plain, ws_form = globals()[entry], globals()[entry + "_ws"]
     if workspace is None:
         st = plain(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
                    num_moduli, md, stream)
     else:
+        if not workspace.is_cuda or workspace.device != A.device:
+            raise ValueError(f"workspace must be a tensor on {A.device}")
         st = ws_form(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
                      num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
     if st:
-        raise Ozaki2Error(st, "ozaki2_sgemm" if single else "ozaki2_dgemm")
+        raise Ozaki2Error(st, entry)
     return C

@@ -200,3 +200,35 @@ def test_zgemm_config_4096_n16():
     ref_i = O.unscale(Xi, er, fc)
     assert_bitwise_equal(np.ascontiguousarray(Cs[:, :, 0].T), ref_r, "sampled Re C")
     assert_bitwise_equal(np.ascontiguousarray(Cs[:, :, 1].T), ref_i, "sampled Im C")
+
+
+@pytest.mark.parametrize("single", [False, True])
+def test_complex_torch_wrappers(single):
+    # row-major torch complex tensors: the wrapper swaps the operands, the
+    # result must equal the oracle's C bit for bit
+    A, B = complex_case(70, 90, 110, seed=31)
+    if single:
+        A, B = A.astype(np.complex64), B.astype(np.complex64)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    fn = oz.cgemm if single else oz.zgemm
+    C = fn(dA, dB, 16).cpu().numpy()
+    r = O.os2_zgemm(A.astype(np.complex128), B.astype(np.complex128), 16, single=single)
+    assert_bitwise_equal(np.ascontiguousarray(C.real), np.ascontiguousarray(r["C"].real), "torch Re C")
+    assert_bitwise_equal(np.ascontiguousarray(C.imag), np.ascontiguousarray(r["C"].imag), "torch Im C")
+    # a caller-provided output and workspace give the same bits
+    out = torch.empty((70, 90), dtype=dA.dtype, device="cuda")
+    ws = torch.empty(oz.ozaki2_zgemm_workspace_size(90, 70, 110, 16), dtype=torch.uint8, device="cuda")
+    fn(dA, dB, 16, out=out, workspace=ws)
+    assert np.array_equal(out.cpu().numpy().view(np.uint8), C.view(np.uint8))
+
+
+def test_torch_wrapper_rejects_bad_out():
+    dA = torch.zeros((8, 5), dtype=torch.float64, device="cuda")
+    dB = torch.zeros((5, 6), dtype=torch.float64, device="cuda")
+    for bad in (torch.empty((6, 8), dtype=torch.float64, device="cuda"),
+                torch.empty((8, 6), dtype=torch.float32, device="cuda"),
+                torch.empty((6, 8), dtype=torch.float64, device="cuda").t()):
+        with pytest.raises(ValueError):
+            oz.dgemm(dA, dB, 8, out=bad)
+    with pytest.raises(TypeError):
+        oz.zgemm(dA, dB, 8)
