@@ -21,9 +21,9 @@ constexpr int kExpEmpty = -4000;          // max-exponent marker of an all-zero 
 
 // Tiling of the packed int8 operands and of the GEMM. A packed operand of R
 // rows and K columns (K a multiple of kKPad) is stored per modulus as
-// [R/32][K/32] fragment blocks of 1 KiB; inside a block, lane L (0..63) owns
-// 16 bytes at L*16 holding row (L % 32) and columns 16*(L / 32) .. +15. This is
-// the operand order of v_mfma_i32_32x32x32_i8, so every global->LDS and
+// [R/16][K/64] fragment blocks of 1 KiB; inside a block, lane L (0..63) owns
+// 16 bytes at L*16 holding row (L % 16) and columns 16*(L / 16) .. +15. This is
+// the operand order of v_mfma_i32_16x16x64_i8, so every global->LDS and
 // LDS->register move is a contiguous 1 KiB per wavefront.
 constexpr int kTileM = 256;   // GEMM block tile rows (A side)
 constexpr int kTileN = 256;   // GEMM block tile columns (B side)

@@ -374,9 +374,11 @@ __global__ __launch_bounds__(256) void k_accurate_exponents(const int32_t *__res
 // Steps 1 + 2: integerize and split into int8 residues (packed MFMA order)
 // ---------------------------------------------------------------------------
 // Block: 32 rows x 128 columns of K, staged through LDS as doubles so that the
-// global reads are coalesced whichever way the source is laid out. Thread t
-// then owns row (t%64)%32 and 16 consecutive K of fragment block t/64, exactly
-// the 16 bytes lane (t%64) holds in the packed layout.
+// global reads are coalesced whichever way the source is laid out. The block
+// covers four fragment blocks of 16 rows x 64 K; wavefront w = t / 64 fills
+// block (row half w % 2, K half w / 2), and lane L owns row L % 16 and the 16
+// consecutive K of quarter L / 16, exactly the 16 bytes it holds in the
+// packed layout.
 constexpr int kSplitRows = 32, kSplitCols = 128, kSplitLd = kSplitCols + 2;
 
 // W parts per element (1 real, 2 complex interleaved); X points at the part.
@@ -444,8 +446,8 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
     split_load_tile<KCONTIG, T>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
 
-    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
-    const int kk0 = fb * 32 + 16 * (lane >> 5);
+    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = (fb & 1) * 16 + (lane & 15);
+    const int kk0 = (fb >> 1) * 64 + 16 * (lane >> 4);
     const int64_t r = r0 + rr;
     int e = r < rows ? ex_row(rr) : 0;
     const bool zero = (e == kExpNonfinite);
@@ -465,7 +467,8 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
         d0[u] = fma(-hi, 0x1p42, x);
     }
 
-    int8_t *dst = out + (bx * kb + by * 4 + fb) * 1024 + lane * 16;
+    const int64_t nkq = kb / 2;  // fragment blocks along K
+    int8_t *dst = out + ((bx * 2 + (fb & 1)) * nkq + by * 2 + (fb >> 1)) * 1024 + lane * 16;
     // modulus 256: x = d0 (mod 256); residue in [-128, 128], 128 and -128 share the low byte
     {
         int v[16];
@@ -501,18 +504,19 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
 // products of Gauss' trick. The sum's residue comes from the exact splits:
 // (d1r + d1i) 2^42 + (d0r + d0i) is the sum with |d0r + d0i| < 2^43, so
 // y = (d1r + d1i)(2^42 mod p) + (d0r + d0i) stays below 2^50.2 and exact.
-// Thread pairs share a lane's 16 bytes (8 K each), so every store of a
-// wavefront covers 512 contiguous bytes. Elements are loaded straight from
-// memory (for A, 32 lanes read 32 consecutive complex rows at one k; for B
-// each thread reads 8 consecutive complex k): no LDS tile.
+// The block covers two fragment blocks (rows 0-15 and 16-31); thread pairs
+// share a lane's 16 bytes (8 K each), so every store of a wavefront covers 512
+// contiguous bytes. Elements are loaded straight from memory (for A, 16 lanes
+// read 16 consecutive complex rows at one k; for B each thread reads 8
+// consecutive complex k): no LDS tile.
 constexpr int kSplitColsC = 64;
 template <bool KCONTIG, class T, class ExpOf>
 __device__ __forceinline__ void split_block_c(const T *__restrict__ X, int64_t rows, int64_t kdim, int64_t ld,
                                               ExpOf ex_row, const SplitConsts &sc, int8_t *__restrict__ out,
                                               int64_t plane_bytes, int64_t kb, int64_t bx, int64_t by) {
-    const int t = threadIdx.x, fb = t >> 7, q = t & 127, lane = q >> 1, half = q & 1, rr = lane & 31;
+    const int t = threadIdx.x, fb = t >> 7, q = t & 127, lane = q >> 1, half = q & 1, rr = fb * 16 + (lane & 15);
     const int64_t r = bx * kSplitRows + rr;
-    const int64_t k0 = by * kSplitColsC + fb * 32 + 16 * (lane >> 5) + 8 * half;
+    const int64_t k0 = by * kSplitColsC + 16 * (lane >> 4) + 8 * half;
     const bool rok = r < rows;
     const int64_t rc = rok ? r : 0;
     double x[2][8];
@@ -542,7 +546,7 @@ __device__ __forceinline__ void split_block_c(const T *__restrict__ X, int64_t r
         d1[2][u] = d1[0][u] + d1[1][u];
         d0[2][u] = d0[0][u] + d0[1][u];
     }
-    int8_t *dst = out + (bx * kb + by * (kSplitColsC / 32) + fb) * 1024 + lane * 16 + 8 * half;
+    int8_t *dst = out + ((bx * 2 + fb) * (kb / 2) + by) * 1024 + lane * 16 + 8 * half;
     for (int l = 0; l < sc.n; ++l) {
         const double p = sc.p[l], pinv = sc.pinv[l], c42 = sc.c42[l];
 #pragma unroll
@@ -619,8 +623,8 @@ __device__ __forceinline__ void quantize_block(double (*tile)[kSplitLd], const T
     const int64_t r0 = bx * kSplitRows, h0 = by * kSplitCols;
     split_load_tile<KCONTIG, T>(tile, X, rows, kdim, ld, r0, h0);
     __syncthreads();
-    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = lane & 31;
-    const int kk0 = fb * 32 + 16 * (lane >> 5);
+    const int t = threadIdx.x, fb = t >> 6, lane = t & 63, rr = (fb & 1) * 16 + (lane & 15);
+    const int kk0 = (fb >> 1) * 64 + 16 * (lane >> 4);
     const int64_t r = r0 + rr;
     int g = r < rows ? gx[r] : 0;
     const bool zero = (g == kExpNonfinite);
@@ -636,7 +640,7 @@ __device__ __forceinline__ void quantize_block(double (*tile)[kSplitLd], const T
     w.y = pack4(v[4], v[5], v[6], v[7]);
     w.z = pack4(v[8], v[9], v[10], v[11]);
     w.w = pack4(v[12], v[13], v[14], v[15]);
-    *(uint4 *)(out + (bx * kb + by * 4 + fb) * 1024 + lane * 16) = w;
+    *(uint4 *)(out + ((bx * 2 + (fb & 1)) * (kb / 2) + by * 2 + (fb >> 1)) * 1024 + lane * 16) = w;
 }
 
 // Both bound operands in one launch: blocks [0, nA) quantize A (row tile
@@ -658,32 +662,35 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 }
 
 // ---------------------------------------------------------------------------
-// Step 3: INT8 GEMM per modulus on v_mfma_i32_32x32x32_i8
+// Step 3: INT8 GEMM per modulus on v_mfma_i32_16x16x64_i8
 // ---------------------------------------------------------------------------
 // Block tile 256 x 256, four wavefronts in 2 x 2, each owning 128 x 128
-// (4 x 4 MFMA tiles, 256 int32 accumulators per lane). K advances 64 bytes per
-// LDS stage (two 32-wide substeps). Stages are copied global -> LDS with
-// global_load_lds_dwordx4 (no VGPR staging) into a ring of kNST buffers, so up
-// to kNST-1 stages are in flight while the MFMAs consume the oldest one.
-// Fragments are double-buffered in registers: the reads for the next substep
-// are issued before the 16 MFMAs of the current one, and the block barrier of
-// a stage is taken before the last substep's MFMAs, whose operands are
-// already in registers. The grid runs over (modulus, tile row, tile column);
-// block ids are remapped so each XCD works through a compact group of tiles of
-// one modulus and its L2 serves the shared A and B panels.
-constexpr int kBK = 64;                    // K bytes per stage
-constexpr int kKS = kBK / 32;              // 32-wide substeps per stage
-constexpr int kNST = 4;                    // LDS stages in the ring
-constexpr int kFA = (kTileM / 32) * kKS;   // A fragment blocks per stage (16)
-constexpr int kFB = (kTileN / 32) * kKS;   // B fragment blocks per stage (16)
+// (8 x 8 MFMA tiles of 16 x 16, 256 int32 accumulators per lane). K advances
+// 64 bytes per LDS stage, one MFMA k-step. Stages are copied global -> LDS
+// with global_load_lds_dwordx4 (no VGPR staging) into a ring of kNST = 5
+// buffers (all 160 KiB of LDS): while the 64 MFMAs of a stage run on
+// fragments already in registers, the wave reads the next stage's 16
+// fragments and issues its 8 copies for the stage kNST - 1 ahead, and the
+// block barrier at the end of the stage leaves two stages in flight. The
+// 16 x 16 x 64 form is used rather than 32 x 32 x 32 because on random
+// residues MI355X sustains more INT8 throughput with it under its power
+// limit (it moves less accumulator data per operation). The grid runs over
+// (modulus, tile row, tile column); block ids are remapped so each XCD works
+// through a compact group of tiles of one modulus and its L2 serves the
+// shared A and B panels.
+constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
+constexpr int kNST = 5;                    // LDS stages in the ring
+constexpr int kFA = kTileM / 16;           // A fragment blocks per stage (16)
+constexpr int kFB = kTileN / 16;           // B fragment blocks per stage (16)
 constexpr int kStageBytes = (kFA + kFB) * 1024;
 constexpr int kLoadsPerWave = (kFA + kFB) / 4;
 constexpr int kGroupM = 4;                 // tile rows per raster group
-constexpr int kReduceStages = 1024;        // 1024 * 64 * 2^14 = 2^30: the range of smod
-static_assert(kKS == 2, "the main loop is written for two substeps per stage");
-// DMA copies a wave may leave in flight at a stage barrier: kNST-2 stages
+constexpr int kReduceStages = 1024;        // stages per launch: 1024 * 64 * 2^14 = 2^30, the range of smod
+static_assert(kNST * kStageBytes <= 160 * 1024, "the ring must fit in LDS");
+// copies a wave may leave in flight at a stage barrier: the kNST - 3 stages
+// after the one the next stage reads
 #define OZ2_GEMM_VMCNT "16"
-static_assert((kNST - 2) * kLoadsPerWave == 16, "OZ2_GEMM_VMCNT must equal (kNST - 2) * kLoadsPerWave");
+static_assert((kNST - 3) * kLoadsPerWave == 16, "OZ2_GEMM_VMCNT must equal (kNST - 3) * kLoadsPerWave");
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -692,6 +699,9 @@ struct GemmArgs {
     const int8_t *RB;
     int64_t planeA, planeB;  // bytes per modulus of RA, RB
     int64_t kb;              // K / 32
+    int64_t ks0;             // first stage (64 K) of this launch
+    int nks;                 // stages of this launch (even)
+    int accumulate;          // EPI_MOD: add the residues already in the planes
     int tiles_m, tiles_n, nmod;  // nmod: operand/output planes (moduli x group)
     int group;                   // planes per modulus: 1 (real) or 3 (complex)
     int64_t m_pad;
@@ -734,195 +744,190 @@ __device__ __forceinline__ int smod(int q, double pinv, int p) {
     return q - __mul24(__double2loint(t), p);
 }
 
-// Step 3 output of one wavefront: its 4 x 4 accumulator tiles reduced mod p
-// and stored with 16-byte stores. A lane's four packed words hold rows
-// {0-3, 8-11, 16-19, 24-27} (lanes 0-31) or {4-7, 12-15, 20-23, 28-31}
-// (lanes 32-63) of its column; lanes L and L + 32 trade two words so that
-// each ends up with 16 consecutive rows.
-__device__ __forceinline__ void store_mod_tiles(const v16i (&acc)[4][4], int p, double pinv, int8_t *plane,
-                                                int64_t m_pad, int row0, int col_base, int lane) {
-    const bool hi = lane >= 32;
+// Step 3 output of one wavefront: its 8 x 8 accumulator tiles reduced mod p
+// and stored with 16-byte stores. In a 16 x 16 tile lane L holds rows
+// 4 (L/16) .. 4 (L/16) + 3 of column L % 16, one packed word; for four tiles
+// stacked in rows, the four lanes L % 16 + 16 q trade words in a 4 x 4
+// transpose (two exchange rounds, across lanes L ^ 32 and L ^ 16) so that
+// each ends with the 16 consecutive rows of one tile.
+__device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][8], int p, double pinv, int8_t *plane,
+                                                int64_t m_pad, int row0, int col0, int lane, bool accumulate) {
+    const bool b1 = (lane >> 5) & 1, b0 = (lane >> 4) & 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint32_t w[4];
+        for (int g = 0; g < 2; ++g) {
+            uint32_t w[4];  // w[c]: rows 4 (L/16) + 0..3 of tile 4g + c
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                w[g] = pack4(smod(acc[i][j][4 * g + 0], pinv, p), smod(acc[i][j][4 * g + 1], pinv, p),
-                             smod(acc[i][j][4 * g + 2], pinv, p), smod(acc[i][j][4 * g + 3], pinv, p));
-            const uint32_t r1 = __shfl_xor(hi ? w[0] : w[2], 32, 64);
-            const uint32_t r2 = __shfl_xor(hi ? w[1] : w[3], 32, 64);
-            const uint4 o = hi ? make_uint4(r1, w[2], r2, w[3]) : make_uint4(w[0], r1, w[1], r2);
-            *(uint4 *)(plane + (int64_t)(col_base + 32 * j) * m_pad + row0 + 32 * i + (hi ? 16 : 0)) = o;
+            for (int c = 0; c < 4; ++c) {
+                const v4i a = acc[4 * g + c][j];
+                w[c] = pack4(smod(a[0], pinv, p), smod(a[1], pinv, p), smod(a[2], pinv, p), smod(a[3], pinv, p));
+            }
+            uint32_t r0 = __shfl_xor(b1 ? w[0] : w[2], 32, 64), r1 = __shfl_xor(b1 ? w[1] : w[3], 32, 64);
+            if (b1) {
+                w[0] = r0;
+                w[1] = r1;
+            } else {
+                w[2] = r0;
+                w[3] = r1;
+            }
+            r0 = __shfl_xor(b0 ? w[0] : w[1], 16, 64);
+            r1 = __shfl_xor(b0 ? w[2] : w[3], 16, 64);
+            if (b0) {
+                w[0] = r0;
+                w[2] = r1;
+            } else {
+                w[1] = r0;
+                w[3] = r1;
+            }
+            // now w[c] = rows 4c .. 4c + 3 of tile 4g + L/16
+            uint4 *dst = (uint4 *)(plane + (int64_t)(col0 + 16 * j + (lane & 15)) * m_pad + row0 +
+                                   16 * (4 * g + (lane >> 4)));
+            if (accumulate) {
+                // a later block of the inner dimension: add the residues of the
+                // earlier blocks (|sum| <= 256) and reduce again
+                const uint4 o = *dst;
+                const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    int r[4];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        r[b] = smod(__builtin_amdgcn_sbfe((int)w[c], 8 * b, 8) + __builtin_amdgcn_sbfe((int)ow[c], 8 * b, 8),
+                                    pinv, p);
+                    w[c] = pack4(r[0], r[1], r[2], r[3]);
+                }
+            }
+            *dst = make_uint4(w[0], w[1], w[2], w[3]);
         }
 }
 
-// KBLK: the inner dimension spans more than kReduceStages stages and the
-// accumulators are folded between blocks (a separate instance, so that the
-// common case carries no fold code and no register spills).
-template <int EPI, bool KBLK>
+// One launch covers stages [ks0, ks0 + nks) of the inner dimension. Longer
+// inner dimensions run in several launches of at most kReduceStages stages
+// (the blocks of [Q] step 3), each adding its residues to those already in the
+// planes, so every int32 sum stays within smod's range.
+template <int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(GemmArgs ga,
                                                                                          ModConsts mc) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * kStageBytes];
 
     int l, tm, tn;
     decode_block(blockIdx.x, gridDim.x, ga.tiles_m, ga.tiles_n, l, tm, tn);
-    // wave index made explicitly wave-uniform so that all DMA addressing below
-    // stays in scalar registers
+    // wave index made explicitly wave-uniform so that all copy addressing
+    // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int wm = wave >> 1, wn = wave & 1;
 
-    v16i acc[4][4];
+    v4i acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v16i){0};
+        for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
-    const int nk = (int)(ga.kb / kKS);
+    const int nk = ga.nks;                              // even
+    const int64_t row_bytes = (ga.kb / 2) * 1024;       // one 16-row block over all of K
 
-    // DMA copy q of a stage (q = 0..7): waves 0-1 copy A fragment blocks, waves
-    // 2-3 B blocks. Source = wave-uniform block address + stage * 2 KiB + lane
-    // * 16; destination = uniform LDS address (M0). Past the last stage the
-    // copy is still issued (from the last stage, into the ring slot that is
-    // never read again) so the main loop has no branch and the counter waits
-    // stay constant.
-    const bool copies_a = wave < (kFA / kLoadsPerWave);
-    const int8_t *dma_base = copies_a
-        ? ga.RA + (int64_t)l * ga.planeA + (int64_t)tm * (kTileM / 32) * ga.kb * 1024
-        : ga.RB + (int64_t)l * ga.planeB + (int64_t)tn * (kTileN / 32) * ga.kb * 1024;
-    // This wave's copies q = 2r, 2r + 1 are the two 32-wide halves (kk = 0, 1)
-    // of fragment row block rb0 + r: a wave-uniform row pointer plus a
-    // per-lane 32-bit offset, so each copy needs one scalar pointer update.
-    const int rb0 = (wave * kLoadsPerWave - (copies_a ? 0 : kFA)) / kKS;
-    const int8_t *dma_row[kLoadsPerWave / kKS];
-#pragma unroll
-    for (int r = 0; r < kLoadsPerWave / kKS; ++r) dma_row[r] = dma_base + (int64_t)(rb0 + r) * ga.kb * 1024;
-    const uint32_t lane_off[kKS] = {(uint32_t)lane * 16, (uint32_t)lane * 16 + 1024};
+    // Copy q of a stage (q = 0..7): waves 0-1 copy A fragment blocks (row
+    // blocks 0-7, 8-15 of the tile), waves 2-3 B blocks. Source = wave-uniform
+    // row block address + stage * 1 KiB + lane * 16; destination = uniform LDS
+    // address (M0). Past the last stage the copy is still issued (from the last
+    // stage, into a ring slot that is never read again) so the main loop has no
+    // branch and the counter waits stay constant.
+    const bool copies_a = wave < 2;
+    const int8_t *dma_base = (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * kFA + (wave & 1) * 8) * row_bytes
+                                       : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * kFB + (wave & 1) * 8) * row_bytes) +
+                             lane * 16;
     __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     auto dma = [&](int ks_slot, int q) {
         const int ks = ks_slot < nk ? ks_slot : nk - 1;
-        const int8_t *src = dma_row[q / kKS] + (int64_t)ks * (kKS * 1024);
-        __builtin_amdgcn_global_load_lds(src + lane_off[q % kKS],
+        __builtin_amdgcn_global_load_lds(dma_base + q * row_bytes + (ga.ks0 + ks) * 1024,
                                          lds3 + (ks_slot % kNST) * kStageBytes + (wave * kLoadsPerWave + q) * 1024,
                                          16, 0, 0);
     };
-    // fragment q of a substep: q < 4 -> A tile q, else B tile q - 4
-    auto frag_ptr = [&](const int8_t *stage, int s, int q) {
-        return q < 4 ? stage + ((wm * 4 + q) * kKS + s) * 1024 + lane * 16
-                     : stage + kFA * 1024 + ((wn * 4 + (q - 4)) * kKS + s) * 1024 + lane * 16;
+    // fragment r of a stage: r < 8 -> A tile r of this wave, else B tile r - 8
+    auto frag = [&](const int8_t *stage, int r) {
+        return *(const v4i *)(stage + (r < 8 ? wm * 8 + r : kFA + wn * 8 + (r - 8)) * 1024 + lane * 16);
     };
 
     // The block barriers below are plain s_barrier with explicit counter waits:
-    // __syncthreads() would also drain every in-flight DMA stage.
+    // __syncthreads() would also drain every in-flight copy.
 #pragma unroll
     for (int st = 0; st < kNST - 1; ++st)
 #pragma unroll
         for (int q = 0; q < kLoadsPerWave; ++q) dma(st, q);
-    asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ")\n\ts_barrier" ::: "memory");  // kNST-2 stages stay in flight
+    asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ")\n\ts_barrier" ::: "memory");  // stages 0 and 1 landed
 
-    v4i f0[8], f1[8];  // fragments of the current / next substep: A tiles 0..3, B tiles 0..3
+    v4i f0[16], f1[16];  // fragments of the current / next stage: A tiles 0..7, B tiles 0..7
 #pragma unroll
-    for (int q = 0; q < 8; ++q) f0[q] = *(const v4i *)frag_ptr(lds, 0, q);
+    for (int r = 0; r < 16; ++r) f0[r] = frag(lds, r);
 
-    // One substep: 16 MFMA slots; slot q also issues fragment read q (q < 8)
-    // of the next substep and, in the first substep of a stage, DMA copy q.
-    // sched_barrier keeps this exact order.
-    const int blk_stages = KBLK ? kReduceStages : nk;
-    for (int ks_blk = 0; ks_blk < nk; ks_blk += blk_stages) {
-        const int ks_end = ks_blk + blk_stages < nk ? ks_blk + blk_stages : nk;
-        for (int ks = ks_blk; ks < ks_end; ++ks) {
-        const int8_t *cur = lds + (ks % kNST) * kStageBytes;
+    // One stage: 64 MFMA slots; every 4th also reads one fragment of the next
+    // stage, every 8th (offset 2) issues one copy. sched_barrier keeps this
+    // exact order. At the end: the stage after next must have landed (it is
+    // read during the next stage) and every read of the next stage's buffer
+    // must be done before a later copy can refill it.
+    auto stage = [&](int ks, v4i(&fc)[16], v4i(&fn)[16]) {
         const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f0[q >> 2], f0[4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
+        for (int q = 0; q < 64; ++q) {
+            acc[q >> 3][q & 7] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q >> 3], fc[8 + (q & 7)], acc[q >> 3][q & 7], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (q < 8) {
-                f1[q] = *(const v4i *)frag_ptr(cur, 1, q);
-                dma(ks + kNST - 1, q);
-            }
+            if ((q & 3) == 0) fn[q >> 2] = frag(nxt, q >> 2);
+            if ((q & 7) == 2) dma(ks + kNST - 1, q >> 3);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // end of stage: the next stage must have landed and every wave must be
-        // done reading this buffer before anyone refills it
         asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // substep 1; reads fetch substep 0 of the next stage (on the last stage
-        // a stale but valid buffer whose values are never used)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f1[q >> 2], f1[4 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            if (q < 8) f0[q] = *(const v4i *)frag_ptr(nxt, 0, q);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        }
-        if (KBLK && EPI == EPI_MOD && ks_end < nk) {
-            // Inner dimension in blocks ([Q] step 3): after 1024 stages
-            // (65536 terms of at most 2^14) fold the sums back to their
-            // symmetric residues, so they stay within smod's range.
-            const int p = (int)mc.p[l / ga.group];
-            const double pinv = mc.pinv[l / ga.group];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[i][j][v] = smod(acc[i][j][v], pinv, p);
-                }
-        }
+    };
+
+    for (int ks = 0; ks < nk; ks += 2) {  // nk is even
+        stage(ks, f0, f1);
+        stage(ks + 1, f1, f0);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
 
-    // Accumulator layout of a 32 x 32 MFMA tile: lane L, register v holds
-    // row 8*(v/4) + 4*(L/32) + v%4, column L%32.
-    const int row_base = tm * kTileM + wm * 128 + 4 * (lane >> 5);
-    const int col_base = tn * kTileN + wn * 128 + (lane & 31);
+    // Accumulator layout of a 16 x 16 MFMA tile: lane L, register v holds row
+    // 4 * (L/16) + v, column L % 16.
+    const int row0 = tm * kTileM + wm * 128, col0 = tn * kTileN + wn * 128;
     if (EPI == EPI_MOD) {
         store_mod_tiles(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
-                        ga.m_pad, tm * kTileM + wm * 128, col_base, lane);
+                        ga.m_pad, row0, col0, lane, ga.accumulate != 0);
     } else if (EPI == EPI_RAW) {
         int32_t *plane = ga.raw + (int64_t)l * ga.plane_elems;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = col_base + 32 * j;
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int row = row_base + 32 * i + 8 * g;
-                    int4 w = make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                       acc[i][j][4 * g + 3]);
-                    *(int4 *)(plane + col * ga.m_pad + row) = w;
-                }
+            for (int j = 0; j < 8; ++j) {
+                const int64_t col = col0 + 16 * j + (lane & 15);
+                const int row = row0 + 16 * i + 4 * (lane >> 4);
+                *(int4 *)(plane + col * ga.m_pad + row) =
+                    make_int4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             }
     } else {  // EPI_BOUND: row and column maxima of the (non-negative) bound product
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
+            for (int v = 0; v < 4; ++v) {
                 int mx = acc[i][0][v];
 #pragma unroll
-                for (int j = 1; j < 4; ++j) mx = max(mx, acc[i][j][v]);
-                // reduce over the 32 lanes that share this row (same lane/32)
+                for (int j = 1; j < 8; ++j) mx = max(mx, acc[i][j][v]);
+                // reduce over the 16 lanes that share this row (same L / 16)
 #pragma unroll
-                for (int off = 16; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
-                if ((lane & 31) == 0) {
-                    const int row = row_base + 32 * i + 8 * (v >> 2) + (v & 3);
-                    atomicMax(&ga.rowmax[row], mx);
-                }
+                for (int off = 8; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
+                if ((lane & 15) == 0) atomicMax(&ga.rowmax[row0 + 16 * i + 4 * (lane >> 4) + v], mx);
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             int mx = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = max(mx, acc[i][j][v]);
+                for (int v = 0; v < 4; ++v) mx = max(mx, acc[i][j][v]);
+            // reduce over the 4 lanes that share this column (same L % 16)
+            mx = max(mx, __shfl_xor(mx, 16, 64));
             mx = max(mx, __shfl_xor(mx, 32, 64));
-            if (lane < 32) atomicMax(&ga.colmax[col_base + 32 * j], mx);
+            if (lane < 16) atomicMax(&ga.colmax[col0 + 16 * j + lane], mx);
         }
     }
 }
@@ -1288,8 +1293,8 @@ __global__ void k_unpack(const int8_t *packed, int64_t rows, int64_t k, int64_t 
     const int64_t l = blockIdx.z;
     if (h >= k) return;
     for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-        const int64_t lane = (r & 31) + 32 * ((h & 31) >> 4);
-        const int64_t off = (((r >> 5) * kb + (h >> 5)) * 64 + lane) * 16 + (h & 15);
+        const int64_t lane = (r & 15) + 16 * ((h & 63) >> 4);
+        const int64_t off = (((r >> 4) * (kb / 2) + (h >> 6)) * 64 + lane) * 16 + (h & 15);
         out[(l * rows + r) * k + h] = packed[l * plane_bytes + off];
     }
 }
@@ -1429,6 +1434,9 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int grou
     g.planeA = L.m_pad * L.k_pad;
     g.planeB = L.n_pad * L.k_pad;
     g.kb = L.kb;
+    g.ks0 = 0;
+    g.nks = (int)(L.kb / 2);
+    g.accumulate = 0;
     g.tiles_m = (int)(L.m_pad / kTileM);
     g.tiles_n = (int)(L.n_pad / kTileN);
     g.nmod = nmod * group;
@@ -1443,12 +1451,16 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
     GemmArgs g = gemm_args(RA, RB, nmod, group, L);
     g.planes = planes;
     const int blocks = g.tiles_m * g.tiles_n * g.nmod;
-    if (g.kb / kKS > kReduceStages) {
-        auto kern = k_gemm<EPI_MOD, true>;
-        OZ2_LAUNCH(ev, kern, dim3(blocks), dim3(256), 0, s, g, mc);
-    } else {
-        auto kern = k_gemm<EPI_MOD, false>;
-        OZ2_LAUNCH(ev, kern, dim3(blocks), dim3(256), 0, s, g, mc);
+    const int64_t nk = L.kb / 2;  // stages of 64 K
+    // blocks of at most kReduceStages stages, the later ones accumulating
+    for (int64_t ks0 = 0; ks0 < nk; ks0 += kReduceStages) {
+        g.ks0 = ks0;
+        g.nks = (int)(nk - ks0 < kReduceStages ? nk - ks0 : kReduceStages);
+        g.accumulate = ks0 > 0;
+        Ev e;
+        if (ks0 == 0) e.start = ev.start;
+        if (ks0 + kReduceStages >= nk) e.stop = ev.stop;
+        OZ2_LAUNCH(e, k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
     }
     return hipGetLastError();
 }
@@ -1459,7 +1471,7 @@ hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int gro
     g.raw = raw;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n * g.nmod;
-    hipLaunchKernelGGL((k_gemm<EPI_RAW, false>), dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
@@ -1470,7 +1482,7 @@ hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *ro
     g.colmax = colmax;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL((k_gemm<EPI_BOUND, false>), dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(256), 0, s, g, mc);
     return hipGetLastError();
 }
 
