@@ -664,33 +664,35 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // ---------------------------------------------------------------------------
 // Step 3: INT8 GEMM per modulus on v_mfma_i32_16x16x64_i8
 // ---------------------------------------------------------------------------
-// Block tile 256 x 256, four wavefronts in 2 x 2, each owning 128 x 128
-// (8 x 8 MFMA tiles of 16 x 16, 256 int32 accumulators per lane). K advances
-// 64 bytes per LDS stage, one MFMA k-step. Stages are copied global -> LDS
-// with global_load_lds_dwordx4 (no VGPR staging) into a ring of kNST = 5
-// buffers (all 160 KiB of LDS): while the 64 MFMAs of a stage run on
-// fragments already in registers, the wave reads the next stage's 16
-// fragments and issues its 8 copies for the stage kNST - 1 ahead, and the
+// Block tile 256 x 256, eight wavefronts in 2 x 4 (two per SIMD), each owning
+// 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32 accumulators per lane).
+// K advances 64 bytes per LDS stage, one MFMA k-step. Stages are copied
+// global -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
+// kNST = 5 buffers (all 160 KiB of LDS): while the 32 MFMAs of a stage run on
+// fragments already in registers, the wave reads the next stage's 12
+// fragments and issues its 4 copies for the stage kNST - 1 ahead, and the
 // block barrier at the end of the stage leaves two stages in flight. The
 // 16 x 16 x 64 form is used rather than 32 x 32 x 32 because on random
 // residues MI355X sustains more INT8 throughput with it under its power
-// limit (it moves less accumulator data per operation). The grid runs over
-// (modulus, tile row, tile column); block ids are remapped so each XCD works
-// through a compact group of tiles of one modulus and its L2 serves the
-// shared A and B panels.
+// limit (it moves less accumulator data per operation), and two waves per
+// SIMD because a wave's LDS reads hardly overlap its own MFMAs while another
+// wave's MFMAs cover them. The grid runs over (modulus, tile row, tile
+// column); block ids are remapped so each XCD works through a compact group
+// of tiles of one modulus and its L2 serves the shared A and B panels.
 constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
 constexpr int kNST = 5;                    // LDS stages in the ring
 constexpr int kFA = kTileM / 16;           // A fragment blocks per stage (16)
 constexpr int kFB = kTileN / 16;           // B fragment blocks per stage (16)
 constexpr int kStageBytes = (kFA + kFB) * 1024;
-constexpr int kLoadsPerWave = (kFA + kFB) / 4;
+constexpr int kGemmWaves = 8;
+constexpr int kLoadsPerWave = (kFA + kFB) / kGemmWaves;  // 4
 constexpr int kGroupM = 4;                 // tile rows per raster group
 constexpr int kReduceStages = 1024;        // stages per launch: 1024 * 64 * 2^14 = 2^30, the range of smod
 static_assert(kNST * kStageBytes <= 160 * 1024, "the ring must fit in LDS");
 // copies a wave may leave in flight at a stage barrier: the kNST - 3 stages
 // after the one the next stage reads
-#define OZ2_GEMM_VMCNT "16"
-static_assert((kNST - 3) * kLoadsPerWave == 16, "OZ2_GEMM_VMCNT must equal (kNST - 3) * kLoadsPerWave");
+#define OZ2_GEMM_VMCNT "8"
+static_assert((kNST - 3) * kLoadsPerWave == 8, "OZ2_GEMM_VMCNT must equal (kNST - 3) * kLoadsPerWave");
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -744,17 +746,17 @@ __device__ __forceinline__ int smod(int q, double pinv, int p) {
     return q - __mul24(__double2loint(t), p);
 }
 
-// Step 3 output of one wavefront: its 8 x 8 accumulator tiles reduced mod p
+// Step 3 output of one wavefront: its 8 x 4 accumulator tiles reduced mod p
 // and stored with 16-byte stores. In a 16 x 16 tile lane L holds rows
 // 4 (L/16) .. 4 (L/16) + 3 of column L % 16, one packed word; for four tiles
 // stacked in rows, the four lanes L % 16 + 16 q trade words in a 4 x 4
 // transpose (two exchange rounds, across lanes L ^ 32 and L ^ 16) so that
 // each ends with the 16 consecutive rows of one tile.
-__device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][8], int p, double pinv, int8_t *plane,
+__device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][4], int p, double pinv, int8_t *plane,
                                                 int64_t m_pad, int row0, int col0, int lane, bool accumulate) {
     const bool b1 = (lane >> 5) & 1, b0 = (lane >> 4) & 1;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             uint32_t w[4];  // w[c]: rows 4 (L/16) + 0..3 of tile 4g + c
@@ -807,8 +809,8 @@ __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][8], int p, d
 // (the blocks of [Q] step 3), each adding its residues to those already in the
 // planes, so every int32 sum stays within smod's range.
 template <int EPI>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm(GemmArgs ga,
-                                                                                         ModConsts mc) {
+__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(GemmArgs ga,
+                                                                                                     ModConsts mc) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * kStageBytes];
 
     int l, tm, tn;
@@ -817,26 +819,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
 
-    v4i acc[8][8];
+    v4i acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+        for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
     const int nk = ga.nks;                              // even
     const int64_t row_bytes = (ga.kb / 2) * 1024;       // one 16-row block over all of K
 
-    // Copy q of a stage (q = 0..7): waves 0-1 copy A fragment blocks (row
-    // blocks 0-7, 8-15 of the tile), waves 2-3 B blocks. Source = wave-uniform
-    // row block address + stage * 1 KiB + lane * 16; destination = uniform LDS
-    // address (M0). Past the last stage the copy is still issued (from the last
-    // stage, into a ring slot that is never read again) so the main loop has no
-    // branch and the counter waits stay constant.
-    const bool copies_a = wave < 2;
-    const int8_t *dma_base = (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * kFA + (wave & 1) * 8) * row_bytes
-                                       : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * kFB + (wave & 1) * 8) * row_bytes) +
+    // Copy q of a stage (q = 0..3): waves 0-3 copy A fragment blocks (row
+    // blocks 4w .. 4w + 3 of the tile), waves 4-7 B blocks. Source =
+    // wave-uniform row block address + stage * 1 KiB + lane * 16; destination =
+    // uniform LDS address (M0). Past the last stage the copy is still issued
+    // (from the last stage, into a ring slot that is never read again) so the
+    // main loop has no branch and the counter waits stay constant.
+    const bool copies_a = wave < 4;
+    const int8_t *dma_base = (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * kFA + (wave & 3) * 4) * row_bytes
+                                       : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * kFB + (wave & 3) * 4) * row_bytes) +
                              lane * 16;
     __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     auto dma = [&](int ks_slot, int q) {
@@ -847,7 +849,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     // fragment r of a stage: r < 8 -> A tile r of this wave, else B tile r - 8
     auto frag = [&](const int8_t *stage, int r) {
-        return *(const v4i *)(stage + (r < 8 ? wm * 8 + r : kFA + wn * 8 + (r - 8)) * 1024 + lane * 16);
+        return *(const v4i *)(stage + (r < 8 ? wm * 8 + r : kFA + wn * 4 + (r - 8)) * 1024 + lane * 16);
     };
 
     // The block barriers below are plain s_barrier with explicit counter waits:
@@ -858,23 +860,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int q = 0; q < kLoadsPerWave; ++q) dma(st, q);
     asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ")\n\ts_barrier" ::: "memory");  // stages 0 and 1 landed
 
-    v4i f0[16], f1[16];  // fragments of the current / next stage: A tiles 0..7, B tiles 0..7
+    v4i f0[12], f1[12];  // fragments of the current / next stage: A tiles 0..7, B tiles 0..3
 #pragma unroll
-    for (int r = 0; r < 16; ++r) f0[r] = frag(lds, r);
+    for (int r = 0; r < 12; ++r) f0[r] = frag(lds, r);
 
-    // One stage: 64 MFMA slots; every 4th also reads one fragment of the next
-    // stage, every 8th (offset 2) issues one copy. sched_barrier keeps this
-    // exact order. At the end: the stage after next must have landed (it is
-    // read during the next stage) and every read of the next stage's buffer
-    // must be done before a later copy can refill it.
-    auto stage = [&](int ks, v4i(&fc)[16], v4i(&fn)[16]) {
+    // One stage: 32 MFMA slots; slots 8u .. 8u + 2 also read fragments
+    // 3u .. 3u + 2 of the next stage, slot 8u + 4 issues copy u.
+    // sched_barrier keeps this exact order. At the end: the stage after next
+    // must have landed (it is read during the next stage) and every read of the
+    // next stage's buffer must be done before a later copy can refill it.
+    auto stage = [&](int ks, v4i(&fc)[12], v4i(&fn)[12]) {
         const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
-            acc[q >> 3][q & 7] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q >> 3], fc[8 + (q & 7)], acc[q >> 3][q & 7], 0, 0, 0);
+        for (int q = 0; q < 32; ++q) {
+            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q >> 2], fc[8 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if ((q & 3) == 0) fn[q >> 2] = frag(nxt, q >> 2);
-            if ((q & 7) == 2) dma(ks + kNST - 1, q >> 3);
+            if ((q & 7) < 3) fn[(q >> 3) * 3 + (q & 7)] = frag(nxt, (q >> 3) * 3 + (q & 7));
+            if ((q & 7) == 4) dma(ks + kNST - 1, q >> 3);
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -888,7 +890,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // Accumulator layout of a 16 x 16 MFMA tile: lane L, register v holds row
     // 4 * (L/16) + v, column L % 16.
-    const int row0 = tm * kTileM + wm * 128, col0 = tn * kTileN + wn * 128;
+    const int row0 = tm * kTileM + wm * 128, col0 = tn * kTileN + wn * 64;
     if (EPI == EPI_MOD) {
         store_mod_tiles(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
                         ga.m_pad, row0, col0, lane, ga.accumulate != 0);
@@ -897,7 +899,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 const int64_t col = col0 + 16 * j + (lane & 15);
                 const int row = row0 + 16 * i + 4 * (lane >> 4);
                 *(int4 *)(plane + col * ga.m_pad + row) =
@@ -910,7 +912,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int v = 0; v < 4; ++v) {
                 int mx = acc[i][0][v];
 #pragma unroll
-                for (int j = 1; j < 8; ++j) mx = max(mx, acc[i][j][v]);
+                for (int j = 1; j < 4; ++j) mx = max(mx, acc[i][j][v]);
                 // reduce over the 16 lanes that share this row (same L / 16)
 #pragma unroll
                 for (int off = 8; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
@@ -918,7 +920,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             int mx = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -1460,7 +1462,7 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
         Ev e;
         if (ks0 == 0) e.start = ev.start;
         if (ks0 + kReduceStages >= nk) e.stop = ev.stop;
-        OZ2_LAUNCH(e, k_gemm<EPI_MOD>, dim3(blocks), dim3(256), 0, s, g, mc);
+        OZ2_LAUNCH(e, k_gemm<EPI_MOD>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
     }
     return hipGetLastError();
 }
@@ -1471,7 +1473,7 @@ hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int gro
     g.raw = raw;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n * g.nmod;
-    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
     return hipGetLastError();
 }
 
@@ -1482,7 +1484,7 @@ hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *ro
     g.colmax = colmax;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(256), 0, s, g, mc);
+    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
     return hipGetLastError();
 }
 
