@@ -87,8 +87,9 @@ enum ozaki2_status {
 #define OZAKI2_MAX_MODULI 20
 /* Inner dimension limits. int32 sums of int8 x int8 products are exact only
  * below 2^17 terms ([Q] section 誤差のないINT8行列積(手順3)); longer inner
- * dimensions are handled in blocks (the GEMM reduces its accumulators mod p
- * every 1024 * 64 terms). The accurate-mode bound product (entries <= 64 * 64
+ * dimensions are handled in blocks (the GEMM reduces each block of at most
+ * 1024 * 64 terms mod p and adds the residues of the blocks). The
+ * accurate-mode bound product (entries <= 64 * 64
  * per term) stays exact below 2^19 terms. */
 #define OZAKI2_MAX_K ((1 << 22) - 1)
 #define OZAKI2_MAX_K_ACCURATE ((1 << 19) - 1)

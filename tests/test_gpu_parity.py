@@ -77,9 +77,9 @@ def test_max_inner_dimension():
                                     (400000, "fast"), ((1 << 17) + 4321, "accurate")])
 def test_long_inner_dimension_in_blocks(k, mode):
     # Beyond 2^17 terms the int32 sums are no longer exact ([Q] step 3: larger
-    # inner dimensions are computed in blocks); the GEMM folds its sums back mod
-    # p every 1024 stages of 64 terms, so 2^16 is the longest unfolded sum and
-    # 2^16 + 64 the shortest folded one.
+    # inner dimensions are computed in blocks); the GEMM runs blocks of at most
+    # 1024 stages of 64 terms, each adding its residues to the earlier ones, so
+    # 2^16 is the longest single block and 2^16 + 64 the shortest split one.
     A, B = W.uniform_case(40, 24, k, seed=k % 97)
     A[0] = 1.0
     B[:, 0] = 1.0  # an all-ones row times an all-ones column: |Q| hits its bound

@@ -17,7 +17,7 @@ import pytest
 
 import oracle as O
 
-Q_MAX = (1 << 30) + 128  # 1024 stages of 64 terms of at most 2^14, plus a folded residue
+Q_MAX = (1 << 30) + 128  # 1024 stages of 64 terms of at most 2^14, plus a carried residue
 
 
 def round_half_even(x: Fraction) -> int:
