@@ -119,11 +119,13 @@ void timing_free_locked() {
     g_timing.used = 0;
 }
 
-// Event and tag slots for one call, or nullptrs when timing is off or full.
-void timing_slots(hipEvent_t **ev, int **tag) {
+// Event and tag slots for one call, or nullptrs when timing is off or full;
+// all_phases is read under the same lock.
+void timing_slots(hipEvent_t **ev, int **tag, bool *all_phases) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     *ev = nullptr;
     *tag = nullptr;
+    *all_phases = g_timing.all_phases;
     if (g_timing.used >= g_timing.max_calls) return;
     const size_t c = (size_t)(g_timing.used++);
     *ev = &g_timing.ev[c * (2 * kMaxIntervals)];
@@ -159,8 +161,8 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
     // time).
     hipEvent_t *ev = nullptr;
     int *tag = nullptr;
-    timing_slots(&ev, &tag);
-    const bool all_phases = g_timing.all_phases;
+    bool all_phases = false;
+    timing_slots(&ev, &tag, &all_phases);
     int nint = 0, open = -1;
     auto ev_of = [&](int phase, bool first, bool last) {
         Ev e;
