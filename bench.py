@@ -2,7 +2,12 @@
 
 One step = one ozaki2_dgemm_ws call (all phases: exponents, residue split,
 INT8 GEMMs, CRT + unscale) on operands already resident in HBM. Prints ONE
-JSON line; see the design doc for the roofline and cpu_baseline definitions.
+JSON line. ``roofline`` rates the dominant kernel (the INT8 GEMM): its N*2mnk
+int8 operations per launch over its average launch time, from HIP events on
+the library's stream in the timed region, against the 5000 TOP/s dense INT8
+peak; ``traffic`` is its HBM bytes per launch from the committed counter
+record while the GEMM source still matches it. ``cpu_baseline`` times the CPU
+oracle on a bounded row sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                        [--mode fast|accurate] [--no-cpu-baseline]
@@ -206,8 +211,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the product would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the product would "
+              "shard by output tiles, with no exchange in fast mode).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

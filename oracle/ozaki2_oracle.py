@@ -28,7 +28,7 @@ Every function below is one of those steps written out plainly, with Python
 integers wherever exactness matters. The heavy loops that need exact 128-bit
 integers or double-double sums live in ``oracle_core.c`` (compiled by gcc).
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * u32, the unit roundoff of binary32, is 2**-24; the margin "4 u32" of [G]
     is kept verbatim.
   * P'_prop (a precomputed constant in [G] section Methodik) is
@@ -582,7 +582,7 @@ def os2_sgemm(A, B, num_moduli: int, mode: str = "fast", e=None, f=None) -> dict
 # Complex products ([G] closing remark: the approach also applies to complex
 # products, ZGEMM/CGEMM, left there as future work)
 # --------------------------------------------------------------------------
-# Reading (each item is listed in the design doc):
+# Reading (where the pages are silent):
 #  * A = Ar + i Ai, B = Br + i Bi. Row i of A takes one exponent, from its
 #    complex 2-norm sum_h (ar^2 + ai^2), with the formula of [G] Methodik;
 #    column j of B likewise. By Cauchy-Schwarz, 2 mu ||a_i|| ||b_j|| nu <= P - 1
