@@ -47,6 +47,9 @@ struct CrtConsts {
     double P32[kChunks];            // P in 32-bit pieces (used for P < 2^128)
     double H32[kChunks];            // P / 2 in 32-bit pieces
     double pinv96;                  // RN(2^96 / P)
+    double pinv64;                  // RN(2^64 / P)
+    double pinv32;                  // RN(2^32 / P)
+    int np32;                       // 32-bit pieces for the digit sums and for P (2..5)
     int nd;                         // signed base-256 digits of the weights (<= kMaxDigits)
     int8_t digit[kMaxDigits][32];   // digit[v][l] = v-th digit of W_l, |digit| <= 128; 0 for l >= n
 };

@@ -947,11 +947,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
 // Pieces of BITS bits: x = sum_t x[t] 2^(BITS t), each x[t] an integer held
 // exactly in a double. normalize brings x[0..2] into [0, 2^BITS) and leaves the
 // signed remainder in x[3].
-template <int BITS>
-__device__ __forceinline__ void normalize4(double x[4]) {
+template <int BITS, int NP = 4>
+__device__ __forceinline__ void normalize4(double x[NP]) {
     constexpr double base = (double)(1ull << BITS), inv = 1.0 / base;
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
+    for (int t = 0; t < NP - 1; ++t) {
         double c = floor(x[t] * inv);
         x[t] = fma(-c, base, x[t]);
         x[t + 1] += c;
@@ -959,32 +959,36 @@ __device__ __forceinline__ void normalize4(double x[4]) {
 }
 
 // sign of a normalized piece vector: -1, 0, +1
-__device__ __forceinline__ int sign4(const double x[4]) {
-    if (x[3] != 0.0) return x[3] > 0.0 ? 1 : -1;
-    return (x[2] != 0.0 || x[1] != 0.0 || x[0] != 0.0) ? 1 : 0;
+template <int NP = 4>
+__device__ __forceinline__ int sign4(const double x[NP]) {
+    if (x[NP - 1] != 0.0) return x[NP - 1] > 0.0 ? 1 : -1;
+    bool nz = false;
+#pragma unroll
+    for (int t = 0; t < NP - 1; ++t) nz = nz || x[t] != 0.0;
+    return nz ? 1 : 0;
 }
 
 // Exact repair of an estimated quotient: bring X into (-P/2, P/2], with P and
 // H = P/2 in the same pieces as x.
-template <int BITS>
-__device__ __forceinline__ void crt_range_fix(double x[4], const double P[4], const double H[4]) {
-    double z[4];
+template <int BITS, int NP = 4>
+__device__ __forceinline__ void crt_range_fix(double x[NP], const double P[], const double H[]) {
+    double z[NP];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) z[t] = x[t] - H[t];
-    normalize4<BITS>(z);
-    if (sign4(z) > 0) {  // X > P/2
+    for (int t = 0; t < NP; ++t) z[t] = x[t] - H[t];
+    normalize4<BITS, NP>(z);
+    if (sign4<NP>(z) > 0) {  // X > P/2
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] -= P[t];
-        normalize4<BITS>(x);
+        for (int t = 0; t < NP; ++t) x[t] -= P[t];
+        normalize4<BITS, NP>(x);
         return;
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) z[t] = x[t] + H[t];
-    normalize4<BITS>(z);
-    if (sign4(z) <= 0) {  // X <= -P/2
+    for (int t = 0; t < NP; ++t) z[t] = x[t] + H[t];
+    normalize4<BITS, NP>(z);
+    if (sign4<NP>(z) <= 0) {  // X <= -P/2
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] += P[t];
-        normalize4<BITS>(x);
+        for (int t = 0; t < NP; ++t) x[t] += P[t];
+        normalize4<BITS, NP>(x);
     }
 }
 
@@ -993,29 +997,29 @@ __device__ __forceinline__ void crt_range_fix(double x[4], const double P[4], co
 // is good to ~2^-37 absolute, so only |S/P - q| within 2^-30 of 1/2 needs the
 // exact wrap check, which valid scalings never reach; the second check catches
 // |X| below ~2^-37 P, where the predicted sign can be wrong.
-template <int BITS>
-__device__ __forceinline__ void crt_lift(const double S[4], double x[4], double &sg, double s_over_base3,
-                                         const double P[4], const double H[4], double pinv_base3) {
+template <int BITS, int NP = 4>
+__device__ __forceinline__ void crt_lift(const double S[NP], double x[NP], double &sg, double s_over_base3,
+                                         const double P[], const double H[], double pinv_base3) {
     const double quo = s_over_base3 * pinv_base3;
     const double q = rint(quo);
     const double d = quo - q;  // ~ X / P
     sg = d < 0.0 ? -1.0 : 1.0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) x[t] = sg * fma(-q, P[t], S[t]);
-    normalize4<BITS>(x);
+    for (int t = 0; t < NP; ++t) x[t] = sg * fma(-q, P[t], S[t]);
+    normalize4<BITS, NP>(x);
     if (fabs(d) > 0.5 - 0x1p-30) {  // near +-P/2: settle the wrap exactly
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] *= sg;
-        crt_range_fix<BITS>(x, P, H);
-        sg = sign4(x) < 0 ? -1.0 : 1.0;
+        for (int t = 0; t < NP; ++t) x[t] *= sg;
+        crt_range_fix<BITS, NP>(x, P, H);
+        sg = sign4<NP>(x) < 0 ? -1.0 : 1.0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] *= sg;
-        normalize4<BITS>(x);
+        for (int t = 0; t < NP; ++t) x[t] *= sg;
+        normalize4<BITS, NP>(x);
     }
-    if (x[3] < 0.0) {  // sign predicted wrongly (|X| tiny)
+    if (x[NP - 1] < 0.0) {  // sign predicted wrongly (|X| tiny)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) x[t] = -x[t];
-        normalize4<BITS>(x);
+        for (int t = 0; t < NP; ++t) x[t] = -x[t];
+        normalize4<BITS, NP>(x);
         sg = -sg;
     }
 }
@@ -1061,15 +1065,16 @@ __device__ __forceinline__ double limbs_to_double(const double x[4], int scale_d
     return ldexp((double)mant, scale - lz + 11 - scale_down);
 }
 
-// The same for a normalized non-negative 32-bit piece vector (x[t] in
-// [0, 2^32)): the top 64 bits of the 128-bit integer with the bits below
+// The same for a normalized non-negative vector of NP (2..4) 32-bit pieces
+// (x[t] in [0, 2^32)): the top 64 bits of the integer with the bits below
 // OR-ed into the last place (round to odd) convert to double with a single
 // rounding, which then equals the rounding of the whole integer (64 >= 53 + 2
 // bits); with ODD the 64 bits are rounded to odd at 53 bits instead.
-template <bool ODD>
-__device__ __forceinline__ double limbs32_to_double(const double x[4], int scale_down) {
+template <bool ODD, int NP = 4>
+__device__ __forceinline__ double limbs32_to_double(const double x[NP], int scale_down) {
     const uint64_t w0 = ((uint64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
-    const uint64_t w1 = ((uint64_t)(uint32_t)x[3] << 32) | (uint32_t)x[2];
+    const uint64_t w1 = NP < 3 ? 0 : ((NP > 3 ? (uint64_t)(uint32_t)x[NP > 3 ? 3 : 0] << 32 : 0) |
+                                      (uint32_t)x[NP > 2 ? 2 : 0]);
     uint64_t top;
     int scale;
     bool odd;
@@ -1105,13 +1110,18 @@ __device__ __forceinline__ OutT crt_finish(const double S[4], int ei, int fj, co
     return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
 
-// As crt_finish for S in 32-bit pieces (P < 2^128, at most 16 moduli).
-template <class OutT>
-__device__ __forceinline__ OutT crt_finish32(const double S[4], int ei, int fj, const CrtConsts &cc) {
-    const double s96 = fma(S[0], 0x1p-96, fma(S[1], 0x1p-64, fma(S[2], 0x1p-32, S[3])));
-    double x[4], sg;
-    crt_lift<32>(S, x, sg, s96, cc.P32, cc.H32, cc.pinv96);
-    const double mag = limbs32_to_double<sizeof(OutT) == 4>(x, ei + fj);
+// As crt_finish for S in NP (2..4) 32-bit pieces, enough for the digit sums
+// and for P (P < 2^(32 NP), at most 16 moduli). The quotient estimate uses
+// S / 2^(32 (NP - 1)) and RN(2^(32 (NP - 1)) / P).
+template <class OutT, int NP = 4>
+__device__ __forceinline__ OutT crt_finish32(const double S[NP], int ei, int fj, const CrtConsts &cc) {
+    double top = S[NP - 1];
+#pragma unroll
+    for (int t = NP - 2; t >= 0; --t) top = fma(S[t], 0x1p-32 * (t == NP - 2 ? 1.0 : t == NP - 3 ? 0x1p-32 : 0x1p-64), top);
+    const double pinv = NP == 4 ? cc.pinv96 : NP == 3 ? cc.pinv64 : cc.pinv32;
+    double x[NP], sg;
+    crt_lift<32, NP>(S, x, sg, top, cc.P32, cc.H32, pinv);
+    const double mag = limbs32_to_double<sizeof(OutT) == 4, NP>(x, ei + fj);
     return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
 
@@ -1165,8 +1175,9 @@ __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, 
 // only in the rows whose half of the accumulator layout ((row / 4) odd or
 // even) matches that k-half, so lane L gets back exactly the 16 digit sums of
 // its own entry, digit v in register v. S is then assembled from the D_v into
-// four exact 32-bit pieces (|piece| < 2^42.1) for crt_finish32.
-template <class OutT>
+// NP exact 32-bit pieces (|piece| < 2^42.1) for crt_finish32; NP = 2 or 3
+// when the weights and P are short (few moduli), which shortens the lift.
+template <class OutT, int NP = 4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_crt_mma(
     const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
     const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
@@ -1210,14 +1221,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
             const v16i D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, R[u], (v16i){0}, 0, 0, 0);
             // 32-bit pieces S_t = D_4t + D_4t+1 2^8 + D_4t+2 2^16 + D_4t+3 2^24:
             // digit pairs in int32 (|.| < 2^26.1), then one exact fma
-            double S[4];
+            double S[NP];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < NP; ++t) {
                 const int lo = D[4 * t] + D[4 * t + 1] * 256, hi = D[4 * t + 2] + D[4 * t + 3] * 256;
                 S[t] = fma((double)hi, 65536.0, (double)lo);
             }
             const int64_t i = i0 + u;
-            if (i < m) C[i + j * ldc] = crt_finish32<OutT>(S, e[i], fj, cc);
+            if (i < m) C[i + j * ldc] = crt_finish32<OutT, NP>(S, e[i], fj, cc);
         }
     }
 }
@@ -1501,8 +1512,8 @@ template <class OutT>
 static hipError_t launch_crt_t(const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                                const CrtConsts &cc, OutT *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev) {
     dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
-    if (cc.n <= 16 && cc.nd <= 16) {
-        auto kern = k_crt_mma<OutT>;
+    if (cc.n <= 16 && cc.nd <= 16 && cc.np32 <= 4) {
+        auto kern = cc.np32 == 2 ? k_crt_mma<OutT, 2> : cc.np32 == 3 ? k_crt_mma<OutT, 3> : k_crt_mma<OutT, 4>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     } else {
         // 17..20 moduli: the 2 x 2 MFMA blocks are mostly padding there, and
