@@ -469,11 +469,17 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
 
     const int64_t nkq = kb / 2;  // fragment blocks along K
     int8_t *dst = out + ((bx * 2 + (fb & 1)) * nkq + by * 2 + (fb >> 1)) * 1024 + lane * 16;
-    // modulus 256: x = d0 (mod 256); residue in [-128, 128], 128 and -128 share the low byte
+    // Only the low byte of a residue is stored, and the symmetric residue r of
+    // an integer y has the low byte of y - k p for k = round(y / p): the low
+    // word of y + 1.5 * 2^52 holds y mod 2^32 (|y| < 2^51, exact), that of
+    // RN(y * RN(1/p) + 1.5 * 2^52) holds k mod 2^32 (y / p is never within
+    // 2^-9 of a half-integer and the product is off by less than 2^-11), and
+    // the 24-bit multiplier keeps k p mod 2^24.
+    // modulus 256: x = d0 (mod 256), the low byte of d0
     {
         int v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = (int)fma(-256.0, rint(d0[u] * 0x1p-8), d0[u]);
+        for (int u = 0; u < 16; ++u) v[u] = __double2loint(d0[u] + 0x1.8p52);
         uint4 w;
         w.x = pack4(v[0], v[1], v[2], v[3]);
         w.y = pack4(v[4], v[5], v[6], v[7]);
@@ -482,12 +488,13 @@ __device__ __forceinline__ void split_block(double (*tile)[kSplitLd], const T *_
         *(uint4 *)dst = w;
     }
     for (int l = 1; l < sc.n; ++l) {
-        const double p = sc.p[l], pinv = sc.pinv[l], c = sc.c42[l];
+        const double pinv = sc.pinv[l], c = sc.c42[l];
+        const int mp = -(int)sc.p[l];
         int v[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            double y = fma(d1[u], c, d0[u]);
-            v[u] = (int)fma(-p, rint(y * pinv), y);
+            const double y = fma(d1[u], c, d0[u]);
+            v[u] = __mul24(__double2loint(fma(y, pinv, 0x1.8p52)), mp) + __double2loint(y + 0x1.8p52);
         }
         uint4 w;
         w.x = pack4(v[0], v[1], v[2], v[3]);
@@ -548,14 +555,17 @@ __device__ __forceinline__ void split_block_c(const T *__restrict__ X, int64_t r
     }
     int8_t *dst = out + ((bx * 2 + fb) * (kb / 2) + by) * 1024 + lane * 16 + 8 * half;
     for (int l = 0; l < sc.n; ++l) {
-        const double p = sc.p[l], pinv = sc.pinv[l], c42 = sc.c42[l];
+        const double pinv = sc.pinv[l], c42 = sc.c42[l];
+        const int mp = -(int)sc.p[l];
 #pragma unroll
         for (int c = 0; c < 3; ++c) {
             int v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const double y = fma(d1[c][u], c42, d0[c][u]);  // p = 256: c42 = 0
-                v[u] = (int)fma(-p, rint(y * pinv), y);
+                // the low byte of y - p round(y / p), as in split_block
+                // (|y| < 2^51; p = 256: c42 = 0 and 1/p is exact)
+                const double y = fma(d1[c][u], c42, d0[c][u]);
+                v[u] = __mul24(__double2loint(fma(y, pinv, 0x1.8p52)), mp) + __double2loint(y + 0x1.8p52);
             }
             uint2 w;
             w.x = pack4(v[0], v[1], v[2], v[3]);
