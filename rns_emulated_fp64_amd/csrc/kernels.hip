@@ -753,7 +753,7 @@ __device__ __forceinline__ void decode_block(int bid, int total, int tiles_m, in
 // byte, where 128 and -128 are the same residue).
 __device__ __forceinline__ int smod(int q, double pinv, int p) {
     const double t = fma((double)q, pinv, 0x1.8p52);
-    return q - __mul24(__double2loint(t), p);
+    return __mul24(__double2loint(t), -p) + q;  // one v_mad_i32_i24
 }
 
 // Step 3 output of one wavefront: its 8 x 4 accumulator tiles reduced mod p
