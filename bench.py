@@ -32,8 +32,11 @@ HBM_PEAK_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # MI355X settles its clock for this load within ~25 ms of a cold start
+    # (the first GEMMs after idle swing between 0.85 and 1.2 ms); 40 warm-up
+    # steps (~50 ms) put the timed region in the sustained state
+    p.add_argument("--steps", type=int, default=40)
+    p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--config", default="spread1.0_4096_n16")
     p.add_argument("--mode", default="fast", choices=["fast", "accurate", "original"],
                    help="original: the comparison stand-in for the original fast-mode rule")
@@ -69,10 +72,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def time_steps(fn, steps, warmup, torch):
-    for _ in range(warmup):
+def time_steps(fn, steps, warmup, torch, settle_ms=60.0):
+    """Mean ms per call of fn over `steps` calls, after at least `warmup`
+    calls and at least `settle_ms` of warm-up (the clock settles under load)."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
         fn()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        done += 1
     t0 = time.perf_counter()
     for _ in range(steps):
         fn()

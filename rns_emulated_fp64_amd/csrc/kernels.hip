@@ -764,7 +764,6 @@ __device__ __forceinline__ int smod(int q, double pinv, int p) {
 // each ends with the 16 consecutive rows of one tile.
 __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][4], int p, double pinv, int8_t *plane,
                                                 int64_t m_pad, int row0, int col0, int lane, bool accumulate) {
-    const bool b1 = (lane >> 5) & 1, b0 = (lane >> 4) & 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -775,23 +774,18 @@ __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][4], int p, d
                 const v4i a = acc[4 * g + c][j];
                 w[c] = pack4(smod(a[0], pinv, p), smod(a[1], pinv, p), smod(a[2], pinv, p), smod(a[3], pinv, p));
             }
-            uint32_t r0 = __shfl_xor(b1 ? w[0] : w[2], 32, 64), r1 = __shfl_xor(b1 ? w[1] : w[3], 32, 64);
-            if (b1) {
-                w[0] = r0;
-                w[1] = r1;
-            } else {
-                w[2] = r0;
-                w[3] = r1;
-            }
-            r0 = __shfl_xor(b0 ? w[0] : w[1], 16, 64);
-            r1 = __shfl_xor(b0 ? w[2] : w[3], 16, 64);
-            if (b0) {
-                w[0] = r0;
-                w[2] = r1;
-            } else {
-                w[1] = r0;
-                w[3] = r1;
-            }
+            // exchange across the wavefront halves, then across the odd and even
+            // rows of 16 lanes: permlane32_swap(x, y) trades x of lanes 32..63
+            // with y of lanes 0..31, permlane16_swap(x, y) x of the odd rows
+            // with y of the even rows
+            const auto h0 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+            const auto h1 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+            const auto q0 = __builtin_amdgcn_permlane16_swap(h0[0], h1[0], false, false);
+            const auto q1 = __builtin_amdgcn_permlane16_swap(h0[1], h1[1], false, false);
+            w[0] = q0[0];
+            w[1] = q0[1];
+            w[2] = q1[0];
+            w[3] = q1[1];
             // now w[c] = rows 4c .. 4c + 3 of tile 4g + L/16
             uint4 *dst = (uint4 *)(plane + (int64_t)(col0 + 16 * j + (lane & 15)) * m_pad + row0 +
                                    16 * (4 * g + (lane >> 4)));
