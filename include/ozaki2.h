@@ -283,17 +283,18 @@ int ozaki2_crt_weight(int num_moduli, int l, uint32_t *out_le32, int out_limbs);
 const char *ozaki2_status_string(int status);
 
 /*
- * Per-phase timing with HIP events recorded on the caller's stream right
- * before and right after each run of consecutive kernels of one phase
- * (phases: 0 scaling/exponents, 1 residue split, 2 INT8 GEMMs, 3 CRT +
- * unscale; fast mode scales and splits A before it scales B, so phases 0 and
- * 1 are each timed as two runs and summed).
+ * Per-phase timing with HIP events on the caller's stream (phases: 0
+ * scaling/exponents, 1 residue split, 2 INT8 GEMMs, 3 CRT + unscale). The
+ * events are attached to the kernel launches themselves
+ * (hipExtLaunchKernelGGL): a phase's start event takes the start time of its
+ * first kernel and its stop event the end time of its last one, so timing
+ * adds no marker packets between kernels.
  * ozaki2_timing_enable(max_calls, all_phases) creates events for up to
  * max_calls product calls (max_calls <= 0 turns timing off); with
- * all_phases == 0 only phase 2 is timed, which keeps the extra stream time to
- * two event records per call. ozaki2_timing_read synchronises them, writes the
- * summed milliseconds per phase to HOST ms_out[4] (0 for untimed phases) and
- * the number of timed calls to *calls, and clears the record.
+ * all_phases == 0 only phase 2 is timed. ozaki2_timing_read synchronises the
+ * events, writes the summed milliseconds per phase to HOST ms_out[4] (0 for
+ * untimed phases) and the number of timed calls to *calls, and clears the
+ * record.
  * Returns 0 or OZAKI2_ERR_HIP.
  */
 int ozaki2_timing_enable(int max_calls, int all_phases);

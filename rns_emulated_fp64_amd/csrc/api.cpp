@@ -155,10 +155,9 @@ struct DebugOut {
 int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
         void *C, int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
     const Tables *T = get_tables(nmod);
-    // Timing events (start/stop per phase) are recorded before the first and
-    // after the last kernel of a phase; unless all phases were asked for, only
-    // the GEMM phase is timed (each record costs a few microseconds of stream
-    // time).
+    // Timing events (start/stop per phase) ride on the first and the last
+    // kernel launch of a phase; unless all phases were asked for, only the
+    // GEMM phase is timed.
     hipEvent_t *ev = nullptr;
     int *tag = nullptr;
     bool all_phases = false;
@@ -467,8 +466,11 @@ int ozaki2_timing_enable(int max_calls, int all_phases) {
     if (max_calls <= 0) return OZAKI2_SUCCESS;
     g_timing.ev.resize((size_t)max_calls * (2 * kMaxIntervals), nullptr);
     g_timing.tag.assign((size_t)max_calls * kMaxIntervals, -1);
+    // The events only measure time (nothing waits on them to read memory), so
+    // they skip the system-scope fence that would flush the caches around the
+    // timed kernels.
     for (hipEvent_t &e : g_timing.ev) {
-        if (hipEventCreate(&e) != hipSuccess) {
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
             e = nullptr;
             timing_free_locked();
             return OZAKI2_ERR_HIP;

@@ -77,8 +77,8 @@ struct Layout {
 
 enum Phase { kPhaseScale = 0, kPhaseSplit = 1, kPhaseGemm = 2, kPhaseCrt = 3, kNumPhases = 4 };
 
-// Optional timing events recorded on the stream right before (start) and
-// right after (stop) one kernel launch.
+// Optional timing events of one kernel launch: start takes the kernel's start
+// time, stop its end time.
 struct Ev {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;

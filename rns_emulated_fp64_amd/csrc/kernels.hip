@@ -18,16 +18,21 @@
 #include <type_traits>
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 
 namespace oz2 {
 
-// Launch with optional timing events recorded right before / after it.
-#define OZ2_LAUNCH(ev, kern, grid, block, shm, stream, ...)              \
-    do {                                                               \
-        if ((ev).start) (void)hipEventRecord((ev).start, stream);      \
-        hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__); \
-        if ((ev).stop) (void)hipEventRecord((ev).stop, stream);        \
+// Launch with optional timing events. hipExtLaunchKernelGGL attaches them to
+// the dispatch itself (start: the kernel's start time, stop: its end time),
+// so a timed launch puts no marker packets in the stream.
+#define OZ2_LAUNCH(ev, kern, grid, block, shm, stream, ...)                                            \
+    do {                                                                                             \
+        if ((ev).start || (ev).stop)                                                                 \
+            hipExtLaunchKernelGGL(kern, grid, block, shm, stream, (ev).start, (ev).stop, 0, __VA_ARGS__); \
+        else                                                                                         \
+            hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);                         \
     } while (0)
 
 typedef int v4i __attribute__((ext_vector_type(4)));

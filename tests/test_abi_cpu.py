@@ -145,3 +145,10 @@ def test_crt_debug_status_codes(args, status):
 def test_status_strings():
     for s in (0, 1, 2, 3, -4, 99):
         assert isinstance(oz.status_string(s), str) and oz.status_string(s)
+
+
+def test_timing_off_and_empty_read_need_no_device():
+    # turning timing off and reading an empty record touch no HIP call
+    oz.ozaki2_timing_enable(0)
+    ms, calls = oz.ozaki2_timing_read()
+    assert calls == 0 and ms == {p: 0.0 for p in oz.PHASES}
