@@ -118,6 +118,9 @@ size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, in
  * As ozaki2_dgemm, with a caller-provided DEVICE workspace of at least
  * ozaki2_workspace_size(...) bytes, 256-byte aligned. Never allocates and is
  * re-entrant; calls that share one workspace must be ordered on one stream.
+ * It only enqueues kernels on the stream (no memset, copy or host
+ * synchronisation), so it can be captured into a HIP graph and replayed;
+ * timing (ozaki2_timing_enable) must be off while capturing.
  * Returns as ozaki2_dgemm; -12 if workspace is NULL (while needed),
  * OZAKI2_ERR_WORKSPACE if workspace_bytes is too small.
  */
