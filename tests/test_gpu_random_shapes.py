@@ -45,3 +45,30 @@ def setup_module(module):
 def test_random_shape(m, n, k, N, mode, phi, pads, seed):
     A, B = W.spread_case(m, n, k, phi, seed=seed)
     full_parity(A, B, N, mode, lda=m + pads[0], ldb=k + pads[1], ldc=m + pads[2], want_prod=True)
+
+
+def _complex_cases(seed=2027, count=16):
+    rng = np.random.default_rng(seed)
+    pick = lambda ranges: int(rng.integers(*ranges[int(rng.integers(len(ranges)))]))
+    out = []
+    for _ in range(count):
+        m = pick([(1, 41), (250, 263)])
+        n = pick([(1, 41), (250, 263)])
+        k = pick([(1, 70), (120, 136), (250, 262)])
+        N = int(rng.integers(2, 21))
+        single = bool(rng.random() < 0.4)
+        pads = [int(x) for x in rng.integers(0, 4, size=3)]
+        out.append((m, n, k, N, single, pads, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k,N,single,pads,seed", _complex_cases(),
+                         ids=lambda v: None if not isinstance(v, tuple) else str(v))
+def test_random_shape_complex(m, n, k, N, single, pads, seed):
+    # complex products (ZGEMM, or CGEMM on binary32 operands): three residue
+    # planes per modulus, every stage bit-exact against the oracle
+    from test_gpu_zgemm import complex_case, complex_parity
+    A, B = complex_case(m, n, k, seed)
+    if single:
+        A, B = A.astype(np.complex64), B.astype(np.complex64)
+    complex_parity(A, B, N, single, lda=m + pads[0], ldb=k + pads[1], ldc=m + pads[2])
