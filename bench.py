@@ -7,7 +7,9 @@ int8 operations per launch over its average launch time, from HIP events on
 the library's stream in the timed region, against the 5000 TOP/s dense INT8
 peak; ``traffic`` is its HBM bytes per launch from the committed counter
 record while the GEMM source still matches it. ``cpu_baseline`` times the CPU
-oracle on a bounded row sample of the same workload.
+oracle on a bounded row sample of the same workload. The default 40 warm-up
+steps put the timed region past the clock transient that follows a cold start
+(the first GEMMs after idle run up to 1.4x slower for about 25 ms).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                        [--mode fast|accurate] [--no-cpu-baseline]
