@@ -279,17 +279,20 @@ def _gemm(A, B, num_moduli, mode, out, workspace, kind):
         if out.dtype != dt or out.device != A.device or tuple(out.shape) != (m, n) or not out.is_contiguous():
             raise ValueError(f"out must be a contiguous ({m}, {n}) {dt} tensor on {A.device}")
         C = out
-    stream = torch.cuda.current_stream(A.device).cuda_stream
     md = _mode(mode)
     plain, ws_form = globals()[entry], globals()[entry + "_ws"]
-    if workspace is None:
-        st = plain(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
-                   num_moduli, md, stream)
-    else:
-        if not workspace.is_cuda or workspace.device != A.device:
-            raise ValueError(f"workspace must be a tensor on {A.device}")
-        st = ws_form(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
-                     num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
+    if workspace is not None and (not workspace.is_cuda or workspace.device != A.device):
+        raise ValueError(f"workspace must be a tensor on {A.device}")
+    # the library launches on the current device: make it the operands' one
+    with torch.cuda.device(A.device):
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        if workspace is None:
+            st = plain(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                       num_moduli, md, stream)
+        else:
+            st = ws_form(n, m, k, B.data_ptr(), max(n, 1), A.data_ptr(), max(k, 1), C.data_ptr(), max(n, 1),
+                         num_moduli, md, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         stream)
     if st:
         raise Ozaki2Error(st, entry)
     return C

@@ -152,3 +152,14 @@ def test_timing_off_and_empty_read_need_no_device():
     oz.ozaki2_timing_enable(0)
     ms, calls = oz.ozaki2_timing_read()
     assert calls == 0 and ms == {p: 0.0 for p in oz.PHASES}
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asking for more exits with a message
+    # before anything touches a device
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
