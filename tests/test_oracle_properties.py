@@ -10,7 +10,8 @@ a wrong sign or index or a transposed operand anywhere along the oracle's
 path fails on some example.
 
 Pages: [Q] the Qiita article on the Chinese remainder theorem and Ozaki
-Scheme II (steps 1-5, sections 中国剰余定理 and 秦九韶の大衍求一術); [G]
+Scheme II (steps 1-5; sections 時計の針で見る定理の中身, 定理が保証すること and
+秦九韶の大衍求一術); [G]
 "Improved Scaling for Fast Mode of Ozaki Scheme II" (section Methodik).
 """
 import math
@@ -67,8 +68,8 @@ def products(draw):
 @SETTINGS
 @given(moduli_subsets, st.data())
 def test_crt_and_garner_recover_every_integer_of_the_symmetric_range(moduli, data):
-    # [Q] 中国剰余定理: residues determine one integer in a range of P
-    # consecutive integers; the oracle reads the range as (-P/2, P/2]
+    # [Q] section 定理が保証すること: residues determine one integer in a range
+    # of P consecutive integers; the oracle reads the range as (-P/2, P/2]
     P = math.prod(moduli)
     X = data.draw(st.integers(-((P - 1) // 2), P // 2))
     c = np.array([[X % p] for p in moduli], dtype=np.int64)
