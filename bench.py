@@ -120,11 +120,16 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
     err = O.error_metrics(Cs[:er].astype(np.float64), hi, lo, A64, B64)
     native = O.error_metrics((A[:er] @ B).astype(np.float64), hi, lo, A64, B64)
     nat = "fp32" if single else "fp64"
+    # the host's native product (numpy / OpenBLAS) on the same sample and cores, as context
+    t0 = time.perf_counter()
+    _ = A[:rows] @ B
+    t_host = time.perf_counter() - t0
     return dict(value=value, unit="TFLOPS", cores=max(omp_threads, blas_threads), kind="oracle",
                 sample=f"rows 0..{rows - 1} of A times all of B ({rows}x{n}x{k}, N={N}, {mode}); "
                        f"{t:.2f} s; OpenMP {omp_threads} threads, BLAS {blas_threads} threads"), \
         dict(parity_mismatches=int(diff.sum()), parity_entries=int(Cs.size), error_rows=er, **err,
-             **{f"native_{nat}_E_cw": native["E_cw"], f"native_{nat}_E_el": native["E_el"]})
+             **{f"native_{nat}_E_cw": native["E_cw"], f"native_{nat}_E_el": native["E_el"],
+                f"host_native_{nat}_gemm_tflops": round(2.0 * rows * n * k / t_host / 1e12, 4)})
 
 
 def cpu_baseline_complex(A, B, C_gpu, N, rows_wanted):
