@@ -56,6 +56,16 @@ def test_tiny_shapes(shape):
     full_parity(A, B, 16, "accurate")
 
 
+@pytest.mark.parametrize("shape", [(70000, 3, 5), (3, 70000, 5), (300, 66000, 2)])
+def test_extreme_aspect_ratios(shape):
+    # n above 65535 exceeds one grid dimension: the kernels that put columns
+    # on the grid's y axis loop over them; m this large gives a long row of
+    # tiles and a single column tile
+    m, n, k = shape
+    A, B = W.uniform_case(m, n, k, seed=m % 1000 + n % 1000)
+    full_parity(A, B, 16, want_prod=False)
+
+
 def test_leading_dimensions():
     A, B = W.spread_case(257, 130, 190, 0.5, seed=3)
     g, r, _ = full_parity(A, B, 16, lda=263, ldb=200, ldc=300)
