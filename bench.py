@@ -247,6 +247,9 @@ def main():
     import rns_emulated_fp64_amd as oz
     import workloads as W
 
+    # a dedicated stream (default priority), current for the whole run: the
+    # library calls, their timing events and the comparators all run on it
+    torch.cuda.set_stream(torch.cuda.Stream(device=torch.device("cuda:0")))
     cfg = W.CONFIGS[args.config]
     if cfg["kind"] == "sweep":
         return sweep_main(args, cfg, torch, oz, W, np)
