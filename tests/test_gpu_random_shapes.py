@@ -72,3 +72,13 @@ def test_random_shape_complex(m, n, k, N, single, pads, seed):
     if single:
         A, B = A.astype(np.complex64), B.astype(np.complex64)
     complex_parity(A, B, N, single, lda=m + pads[0], ldb=k + pads[1], ldc=m + pads[2])
+
+
+@pytest.mark.parametrize("m,n,k,N,mode,phi,pads,seed", _cases(seed=2028, count=16),
+                         ids=lambda v: None if not isinstance(v, tuple) else str(v))
+def test_random_shape_single(m, n, k, N, mode, phi, pads, seed):
+    # binary32 operands through ozaki2_sgemm_debug: every stage bit-exact,
+    # C rounded once to binary32 as the oracle's os2_sgemm does
+    A, B = W.spread_case(m, n, k, phi, seed=seed)
+    full_parity(A.astype(np.float32), B.astype(np.float32), N, mode, lda=m + pads[0], ldb=k + pads[1],
+                ldc=m + pads[2], want_prod=True)
