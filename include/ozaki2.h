@@ -37,6 +37,10 @@
  *   stream    hipStream_t to enqueue on (NULL = default stream). All device
  *             work is asynchronous; no call synchronises the stream.
  *
+ * Environment: OZ2_GEMM_TILE=128 or 256 forces the INT8 GEMM's block shape
+ * (by default 256 x 256, or 128 x 128 for products too small to give every
+ * two compute units a 256 x 256 block); results do not depend on it.
+ *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by
  * ozaki2_finalize) and small per-device constant tables.

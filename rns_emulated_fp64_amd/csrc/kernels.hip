@@ -15,8 +15,12 @@
 // own unless an fma() is written out, which the exact integer arithmetic
 // relies on.
 #include <float.h>
-#include <type_traits>
 #include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -714,7 +718,9 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // Step 3: INT8 GEMM per modulus on v_mfma_i32_16x16x64_i8
 // ---------------------------------------------------------------------------
 // Block tile 256 x 256, eight wavefronts in 2 x 4 (two per SIMD), each owning
-// 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32 accumulators per lane).
+// 128 x 64 (8 x 4 MFMA tiles of 16 x 16, 128 int32 accumulators per lane);
+// for products too small to give every CU two such tiles, a 128 x 128 tile of
+// four wavefronts (64 x 64 each, two blocks per CU) with the same schedule.
 // K advances 64 bytes per LDS stage, one MFMA k-step. Stages are copied
 // global -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
 // kNST = 5 buffers (all 160 KiB of LDS): while the 32 MFMAs of a stage run on
@@ -730,18 +736,31 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // of tiles of one modulus and its L2 serves the shared A and B panels.
 constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
 constexpr int kNST = 5;                    // LDS stages in the ring
-constexpr int kFA = kTileM / 16;           // A fragment blocks per stage (16)
-constexpr int kFB = kTileN / 16;           // B fragment blocks per stage (16)
-constexpr int kStageBytes = (kFA + kFB) * 1024;
-constexpr int kGemmWaves = 8;
-constexpr int kLoadsPerWave = (kFA + kFB) / kGemmWaves;  // 4
+constexpr int kLoadsPerWave = 4;           // 1 KiB copies per wave per stage (both tile shapes)
 constexpr int kGroupM = 4;                 // tile rows per raster group
 constexpr int kReduceStages = 1024;        // stages per launch: 1024 * 64 * 2^14 = 2^30, the range of smod
-static_assert(kNST * kStageBytes <= 160 * 1024, "the ring must fit in LDS");
 // copies a wave may leave in flight at a stage barrier: the kNST - 3 stages
 // after the one the next stage reads
 #define OZ2_GEMM_VMCNT "8"
 static_assert((kNST - 3) * kLoadsPerWave == 8, "OZ2_GEMM_VMCNT must equal (kNST - 3) * kLoadsPerWave");
+
+// A block shape: WM x WN wavefronts, each owning RT x CT MFMA tiles of 16 x 16.
+template <int WM_, int WN_, int RT_, int CT_>
+struct GemmShape {
+    static constexpr int WM = WM_, WN = WN_, RT = RT_, CT = CT_;
+    static constexpr int W = WM * WN;                        // wavefronts per block
+    static constexpr int TM = WM * RT * 16, TN = WN * CT * 16;  // block tile
+    static constexpr int FA = TM / 16, FB = TN / 16;         // fragment blocks per stage
+    static constexpr int STAGE = (FA + FB) * 1024;           // bytes per LDS stage
+    static constexpr int NF = RT + CT;                       // fragments a wave reads per stage
+    static constexpr int NQ = RT * CT;                       // MFMAs per wave per stage
+    static_assert(FA == FB && FA == (W / 2) * kLoadsPerWave, "half the waves copy A, half B");
+    static_assert(kNST * STAGE <= 160 * 1024, "the ring must fit in LDS");
+    static_assert(NQ % kLoadsPerWave == 0 && NF % kLoadsPerWave == 0, "copies and reads spread evenly");
+    static_assert(RT % 4 == 0, "the epilogue transposes groups of four row tiles");
+};
+using ShapeL = GemmShape<2, 4, 8, 4>;  // 256 x 256, 8 waves of 128 x 64
+using ShapeS = GemmShape<2, 2, 4, 4>;  // 128 x 128, 4 waves of 64 x 64
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -801,12 +820,13 @@ __device__ __forceinline__ int smod(int q, double pinv, int p) {
 // stacked in rows, the four lanes L % 16 + 16 q trade words in a 4 x 4
 // transpose (two exchange rounds, across lanes L ^ 32 and L ^ 16) so that
 // each ends with the 16 consecutive rows of one tile.
-__device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][4], int p, double pinv, int8_t *plane,
+template <int RT, int CT>
+__device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[RT][CT], int p, double pinv, int8_t *plane,
                                                 int64_t m_pad, int row0, int col0, int lane, bool accumulate) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < CT; ++j)
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < RT / 4; ++g) {
             uint32_t w[4];  // w[c]: rows 4 (L/16) + 0..3 of tile 4g + c
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -851,10 +871,11 @@ __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[8][4], int p, d
 // inner dimensions run in several launches of at most kReduceStages stages
 // (the blocks of [Q] step 3), each adding its residues to those already in the
 // planes, so every int32 sum stays within smod's range.
-template <int EPI>
-__global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(GemmArgs ga,
-                                                                                                     ModConsts mc) {
-    __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * kStageBytes];
+template <int EPI, class SH>
+__global__ __launch_bounds__(64 * SH::W) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_gemm(GemmArgs ga,
+                                                                                                ModConsts mc) {
+    constexpr int RT = SH::RT, CT = SH::CT, NF = SH::NF, NQ = SH::NQ, FA = SH::FA, STAGE = SH::STAGE;
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * STAGE];
 
     int l, tm, tn;
     decode_block(blockIdx.x, gridDim.x, ga.tiles_m, ga.tiles_n, l, tm, tn);
@@ -862,37 +883,38 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
     // below stays in scalar registers
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / SH::WN, wn = wave % SH::WN;
 
-    v4i acc[8][4];
+    v4i acc[RT][CT];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+        for (int j = 0; j < CT; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 
     const int nk = ga.nks;                              // even
     const int64_t row_bytes = (ga.kb / 2) * 1024;       // one 16-row block over all of K
 
-    // Copy q of a stage (q = 0..3): waves 0-3 copy A fragment blocks (row
-    // blocks 4w .. 4w + 3 of the tile), waves 4-7 B blocks. Source =
+    // Copy q of a stage (q = 0..3): the first half of the waves copy A
+    // fragment blocks (row blocks 4w .. 4w + 3 of the tile), the rest B blocks. Source =
     // wave-uniform row block address + stage * 1 KiB + lane * 16; destination =
     // uniform LDS address (M0). Past the last stage the copy is still issued
     // (from the last stage, into a ring slot that is never read again) so the
     // main loop has no branch and the counter waits stay constant.
-    const bool copies_a = wave < 4;
-    const int8_t *dma_base = (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * kFA + (wave & 3) * 4) * row_bytes
-                                       : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * kFB + (wave & 3) * 4) * row_bytes) +
+    const bool copies_a = wave < SH::W / 2;
+    const int wq = wave % (SH::W / 2);
+    const int8_t *dma_base = (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * FA + wq * 4) * row_bytes
+                                       : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * SH::FB + wq * 4) * row_bytes) +
                              lane * 16;
     __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     auto dma = [&](int ks_slot, int q) {
         const int ks = ks_slot < nk ? ks_slot : nk - 1;
         __builtin_amdgcn_global_load_lds(dma_base + q * row_bytes + (ga.ks0 + ks) * 1024,
-                                         lds3 + (ks_slot % kNST) * kStageBytes + (wave * kLoadsPerWave + q) * 1024,
+                                         lds3 + (ks_slot % kNST) * STAGE + (wave * kLoadsPerWave + q) * 1024,
                                          16, 0, 0);
     };
-    // fragment r of a stage: r < 8 -> A tile r of this wave, else B tile r - 8
+    // fragment r of a stage: r < RT -> A tile r of this wave, else B tile r - RT
     auto frag = [&](const int8_t *stage, int r) {
-        return *(const v4i *)(stage + (r < 8 ? wm * 8 + r : kFA + wn * 4 + (r - 8)) * 1024 + lane * 16);
+        return *(const v4i *)(stage + (r < RT ? wm * RT + r : FA + wn * CT + (r - RT)) * 1024 + lane * 16);
     };
 
     // The block barriers below are plain s_barrier with explicit counter waits:
@@ -903,23 +925,25 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
         for (int q = 0; q < kLoadsPerWave; ++q) dma(st, q);
     asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ")\n\ts_barrier" ::: "memory");  // stages 0 and 1 landed
 
-    v4i f0[12], f1[12];  // fragments of the current / next stage: A tiles 0..7, B tiles 0..3
+    v4i f0[NF], f1[NF];  // fragments of the current / next stage: A tiles, then B tiles
 #pragma unroll
-    for (int r = 0; r < 12; ++r) f0[r] = frag(lds, r);
+    for (int r = 0; r < NF; ++r) f0[r] = frag(lds, r);
 
-    // One stage: 32 MFMA slots; slots 8u .. 8u + 2 also read fragments
-    // 3u .. 3u + 2 of the next stage, slot 8u + 4 issues copy u.
+    // One stage: NQ MFMA slots in 4 groups of SG; the first RG slots of group
+    // u also read fragments RG u .. RG u + RG - 1 of the next stage, slot
+    // SG / 2 of group u issues copy u (256 x 256: 8 slots, 3 reads).
     // sched_barrier keeps this exact order. At the end: the stage after next
     // must have landed (it is read during the next stage) and every read of the
     // next stage's buffer must be done before a later copy can refill it.
-    auto stage = [&](int ks, v4i(&fc)[12], v4i(&fn)[12]) {
-        const int8_t *nxt = lds + ((ks + 1) % kNST) * kStageBytes;
+    constexpr int SG = NQ / kLoadsPerWave, RG = NF / kLoadsPerWave;
+    auto stage = [&](int ks, v4i(&fc)[NF], v4i(&fn)[NF]) {
+        const int8_t *nxt = lds + ((ks + 1) % kNST) * STAGE;
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q >> 2], fc[8 + (q & 3)], acc[q >> 2][q & 3], 0, 0, 0);
+        for (int q = 0; q < NQ; ++q) {
+            acc[q / CT][q % CT] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q / CT], fc[RT + q % CT], acc[q / CT][q % CT], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if ((q & 7) < 3) fn[(q >> 3) * 3 + (q & 7)] = frag(nxt, (q >> 3) * 3 + (q & 7));
-            if ((q & 7) == 4) dma(ks + kNST - 1, q >> 3);
+            if ((q % SG) < RG) fn[(q / SG) * RG + (q % SG)] = frag(nxt, (q / SG) * RG + (q % SG));
+            if ((q % SG) == SG / 2) dma(ks + kNST - 1, q / SG);
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt vmcnt(" OZ2_GEMM_VMCNT ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -933,16 +957,16 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
 
     // Accumulator layout of a 16 x 16 MFMA tile: lane L, register v holds row
     // 4 * (L/16) + v, column L % 16.
-    const int row0 = tm * kTileM + wm * 128, col0 = tn * kTileN + wn * 64;
+    const int row0 = tm * SH::TM + wm * RT * 16, col0 = tn * SH::TN + wn * CT * 16;
     if (EPI == EPI_MOD) {
         store_mod_tiles(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group], ga.planes + (int64_t)l * ga.plane_elems,
                         ga.m_pad, row0, col0, lane, ga.accumulate != 0);
     } else if (EPI == EPI_RAW) {
         int32_t *plane = ga.raw + (int64_t)l * ga.plane_elems;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < CT; ++j) {
                 const int64_t col = col0 + 16 * j + (lane & 15);
                 const int row = row0 + 16 * i + 4 * (lane >> 4);
                 *(int4 *)(plane + col * ga.m_pad + row) =
@@ -950,12 +974,12 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
             }
     } else {  // EPI_BOUND: row and column maxima of the (non-negative) bound product
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < RT; ++i) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 int mx = acc[i][0][v];
 #pragma unroll
-                for (int j = 1; j < 4; ++j) mx = max(mx, acc[i][j][v]);
+                for (int j = 1; j < CT; ++j) mx = max(mx, acc[i][j][v]);
                 // reduce over the 16 lanes that share this row (same L / 16)
 #pragma unroll
                 for (int off = 8; off >= 1; off >>= 1) mx = max(mx, __shfl_xor(mx, off, 64));
@@ -963,10 +987,10 @@ __global__ __launch_bounds__(64 * kGemmWaves) __attribute__((amdgpu_waves_per_eu
             }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < CT; ++j) {
             int mx = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) mx = max(mx, acc[i][j][v]);
             // reduce over the 4 lanes that share this column (same L % 16)
@@ -1487,7 +1511,31 @@ hipError_t launch_quantize(Elem el, const void *A, int64_t m, int64_t lda, const
     return launch_quantize_t((const double *)A, m, lda, (const double *)B, n, ldb, k, L, ws, s);
 }
 
-static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L) {
+// Tile shape of a product: 256 x 256 unless that gives at most one block per
+// two compute units, then 128 x 128 (four times the blocks; on MI355X it was
+// 1.2-1.9x faster up to that point and slower beyond it, where its larger LDS
+// traffic per MFMA costs more than the fuller chip gains). OZ2_GEMM_TILE=128
+// or 256 in the environment forces a shape; the results do not depend on it
+// (the tests run both shapes at every size).
+static bool use_small_tiles(const Layout &L, int planes) {
+    if (const char *force = getenv("OZ2_GEMM_TILE")) {
+        if (strcmp(force, "128") == 0) return true;
+        if (strcmp(force, "256") == 0) return false;
+    }
+    static std::atomic<int> cu_count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int cus = cu_count[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    const int64_t blocks = (L.m_pad / ShapeL::TM) * (L.n_pad / ShapeL::TN) * (int64_t)planes;
+    return 2 * blocks <= (int64_t)cus;
+}
+
+static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L, bool small) {
     GemmArgs g{};
     g.RA = RA;
     g.RB = RB;
@@ -1497,8 +1545,8 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int grou
     g.ks0 = 0;
     g.nks = (int)(L.kb / 2);
     g.accumulate = 0;
-    g.tiles_m = (int)(L.m_pad / kTileM);
-    g.tiles_n = (int)(L.n_pad / kTileN);
+    g.tiles_m = (int)(L.m_pad / (small ? ShapeS::TM : ShapeL::TM));
+    g.tiles_n = (int)(L.n_pad / (small ? ShapeS::TN : ShapeL::TN));
     g.nmod = nmod * group;
     g.group = group;
     g.m_pad = L.m_pad;
@@ -1508,7 +1556,8 @@ static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int grou
 
 hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int group, const ModConsts &mc,
                            int8_t *planes, const Layout &L, hipStream_t s, Ev ev) {
-    GemmArgs g = gemm_args(RA, RB, nmod, group, L);
+    const bool small = use_small_tiles(L, nmod * group);
+    GemmArgs g = gemm_args(RA, RB, nmod, group, L, small);
     g.planes = planes;
     const int blocks = g.tiles_m * g.tiles_n * g.nmod;
     const int64_t nk = L.kb / 2;  // stages of 64 K
@@ -1520,29 +1569,43 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
         Ev e;
         if (ks0 == 0) e.start = ev.start;
         if (ks0 + kReduceStages >= nk) e.stop = ev.stop;
-        OZ2_LAUNCH(e, k_gemm<EPI_MOD>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
+        if (small) {
+            auto kern = k_gemm<EPI_MOD, ShapeS>;
+            OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
+        } else {
+            auto kern = k_gemm<EPI_MOD, ShapeL>;
+            OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeL::W), 0, s, g, mc);
+        }
     }
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_raw(const int8_t *RA, const int8_t *RB, int nmod, int group, int32_t *raw, const Layout &L,
                            hipStream_t s) {
-    GemmArgs g = gemm_args(RA, RB, nmod, group, L);
+    const bool small = use_small_tiles(L, nmod * group);
+    GemmArgs g = gemm_args(RA, RB, nmod, group, L, small);
     g.raw = raw;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n * g.nmod;
-    hipLaunchKernelGGL(k_gemm<EPI_RAW>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
+    if (small)
+        hipLaunchKernelGGL((k_gemm<EPI_RAW, ShapeS>), dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
+    else
+        hipLaunchKernelGGL((k_gemm<EPI_RAW, ShapeL>), dim3(blocks), dim3(64 * ShapeL::W), 0, s, g, mc);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bound(const int8_t *Abar, const int8_t *Bbar, int32_t *rowmax, int32_t *colmax,
                              const Layout &L, hipStream_t s) {
-    GemmArgs g = gemm_args(Abar, Bbar, 1, 1, L);
+    const bool small = use_small_tiles(L, 1);
+    GemmArgs g = gemm_args(Abar, Bbar, 1, 1, L, small);
     g.rowmax = rowmax;
     g.colmax = colmax;
     ModConsts mc{};
     const int blocks = g.tiles_m * g.tiles_n;
-    hipLaunchKernelGGL(k_gemm<EPI_BOUND>, dim3(blocks), dim3(64 * kGemmWaves), 0, s, g, mc);
+    if (small)
+        hipLaunchKernelGGL((k_gemm<EPI_BOUND, ShapeS>), dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
+    else
+        hipLaunchKernelGGL((k_gemm<EPI_BOUND, ShapeL>), dim3(blocks), dim3(64 * ShapeL::W), 0, s, g, mc);
     return hipGetLastError();
 }
 

@@ -82,3 +82,14 @@ def test_random_shape_single(m, n, k, N, mode, phi, pads, seed):
     A, B = W.spread_case(m, n, k, phi, seed=seed)
     full_parity(A.astype(np.float32), B.astype(np.float32), N, mode, lda=m + pads[0], ldb=k + pads[1],
                 ldc=m + pads[2], want_prod=True)
+
+
+@pytest.mark.parametrize("tile", ["128", "256"])
+@pytest.mark.parametrize("m,n,k,N,mode,phi,pads,seed", _cases(seed=2029, count=8),
+                         ids=lambda v: None if not isinstance(v, tuple) else str(v))
+def test_random_shape_each_tile_shape(monkeypatch, tile, m, n, k, N, mode, phi, pads, seed):
+    # the GEMM has a 256 x 256 and a 128 x 128 block shape, chosen by problem
+    # size; forcing each one here runs both on every shape
+    monkeypatch.setenv("OZ2_GEMM_TILE", tile)
+    A, B = W.spread_case(m, n, k, phi, seed=seed)
+    full_parity(A, B, N, mode, lda=m + pads[0], ldb=k + pads[1], ldc=m + pads[2], want_prod=True)
