@@ -51,21 +51,35 @@ def parse():
     return p.parse_args()
 
 
+def gemm_source_hash():
+    """SHA-256 of the GEMM's source (its section of kernels.hip and common.h)
+    with comments and blank lines removed: it changes when the code does, not
+    when only its comments do."""
+    import hashlib
+    import re
+
+    def code(src):
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        lines = [re.sub(r"//.*$", "", line).rstrip() for line in src.splitlines()]
+        return "\n".join(line for line in lines if line.strip())
+
+    src = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "kernels.hip")).read()
+    sec = src[src.index("// Step 3: INT8 GEMM"):src.index("// Steps 4 + 5")]
+    common = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "common.h")).read()
+    return hashlib.sha256((code(sec) + "\n" + code(common)).encode()).hexdigest()
+
+
 def gemm_traffic_bytes():
     """HBM bytes per GEMM launch from the committed counter runs, or None.
 
-    The figure is used only while the GEMM source still hashes to the one the
+    The figure is used only while the GEMM's code still hashes to the one the
     counters were taken on.
     """
-    import hashlib
     path = os.path.join(ROOT, "profiles", "k_gemm_spread1.0_4096_n16_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "kernels.hip")).read()
-    sec = src[src.index("// Step 3: INT8 GEMM"):src.index("// Steps 4 + 5")]
-    common = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "common.h")).read()
-    if hashlib.sha256((sec + common).encode()).hexdigest() != rec["gemm_source_sha256"]:
+    if gemm_source_hash() != rec["gemm_code_sha256"]:
         return None
     return float(rec["traffic_bytes_per_launch"])
 

@@ -25,8 +25,8 @@ constexpr int kExpEmpty = -4000;          // max-exponent marker of an all-zero 
 // 16 bytes at L*16 holding row (L % 16) and columns 16*(L / 16) .. +15. This is
 // the operand order of v_mfma_i32_16x16x64_i8, so every global->LDS and
 // LDS->register move is a contiguous 1 KiB per wavefront.
-constexpr int kTileM = 256;   // GEMM block tile rows (A side)
-constexpr int kTileN = 256;   // GEMM block tile columns (B side)
+constexpr int kTileM = 256;   // row padding of A (the GEMM's largest block tile; 128 divides it)
+constexpr int kTileN = 256;   // column padding of B
 constexpr int kKPad = 128;    // K padding granule (split kernel tile width)
 
 // Host-computed constants for the residue split ([Q] steps 1 and 2).

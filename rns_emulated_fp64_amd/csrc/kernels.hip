@@ -723,9 +723,10 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // four wavefronts (64 x 64 each, two blocks per CU) with the same schedule.
 // K advances 64 bytes per LDS stage, one MFMA k-step. Stages are copied
 // global -> LDS with global_load_lds_dwordx4 (no VGPR staging) into a ring of
-// kNST = 5 buffers (all 160 KiB of LDS): while the 32 MFMAs of a stage run on
-// fragments already in registers, the wave reads the next stage's 12
-// fragments and issues its 4 copies for the stage kNST - 1 ahead, and the
+// kNST = 5 buffers (all 160 KiB of LDS; 80 KiB for the small shape): while the
+// 32 MFMAs of a stage run on fragments already in registers (16 in the small
+// shape), the wave reads the next stage's 12 fragments (8) and issues its 4
+// copies for the stage kNST - 1 ahead, and the
 // block barrier at the end of the stage leaves two stages in flight. The
 // 16 x 16 x 64 form is used rather than 32 x 32 x 32 because on random
 // residues MI355X sustains more INT8 throughput with it under its power
