@@ -67,7 +67,7 @@ def scale_sweep_case(size: int = 2048, seed: int = 0):
     return np.ones((size, size)), ua, b
 
 
-#: The five workloads: name -> (m, n, k, N moduli, generator kwargs).
+#: The workloads: name -> (m, n, k, N moduli, generator kwargs).
 CONFIGS = {
     # 64^3, U(-1,1), N=8, fast mode: small enough for the oracle in well under a second.
     "u64_n8": dict(m=64, n=64, k=64, num_moduli=8, kind="uniform", seed=0),
@@ -75,6 +75,8 @@ CONFIGS = {
     "spread0.5_1024_n14": dict(m=1024, n=1024, k=1024, num_moduli=14, kind="spread", phi=0.5, seed=0),
     # 4096^3, wide exponent spread phi=1.0, N=16: the headline workload.
     "spread1.0_4096_n16": dict(m=4096, n=4096, k=4096, num_moduli=16, kind="spread", phi=1.0, seed=0),
+    # 512^3, phi=1.0, N=14: a small product (the GEMM's 128 x 128 block shape).
+    "spread1.0_512_n14": dict(m=512, n=512, k=512, num_moduli=14, kind="spread", phi=1.0, seed=0),
     # 2048^3 scale sweep, N=14.
     "scale_sweep_2048_n14": dict(m=2048, n=2048, k=2048, num_moduli=14, kind="sweep", seed=0),
     # 16384^3, phi=1.0, N=18 (2 GiB per operand).
