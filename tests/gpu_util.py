@@ -102,15 +102,23 @@ def to_oracle_exponents(v: np.ndarray) -> list:
 
 
 def exponent_is_valid(row: np.ndarray, e: int, Pp: float) -> bool:
-    """e <= floor(P' - 0.5 (log2 sum row^2 + 4 u32)) + 1 within a 2^-40 band of the boundary."""
+    """Is e the fast-mode exponent of row, up to rounding at the boundary?
+
+    z = P' - 0.5 (log2 sum row^2 + 4 u32) is evaluated at 60 digits. Away
+    from an integer e must be floor(z). Within 2^-40 of an integer n (where
+    the two sides' summation orders and log2 routines may round z to either
+    side) e may be n - 1 or n, never n + 1: an exponent above floor(z + 2^-40)
+    would break the bound of [G] Methodik by more than rounding.
+    """
     with mpmath.workdps(60):
         s = mpmath.fsum(mpmath.mpf(float(x)) ** 2 for x in row)
         if s == 0:
             return e == 0
         z = mpmath.mpf(Pp) - (mpmath.log(s, 2) + 4 * mpmath.mpf(O.U32)) / 2
-        fl = int(mpmath.floor(z))
-        near = abs(z - mpmath.nint(z)) < mpmath.mpf(2) ** -40
-        return e == fl or (near and e in (fl - 1, fl + 1))
+        n = int(mpmath.nint(z))
+        if abs(z - n) < mpmath.mpf(2) ** -40:
+            return e in (n - 1, n)
+        return e == int(mpmath.floor(z))
 
 
 def reconcile_exponents(gpu_e: np.ndarray, orc_e: list, X: np.ndarray, N: int, mode: str):

@@ -36,6 +36,14 @@ def test_nm_lists_symbols():
         assert re.search(rf"\bT {name}\b", out), name
 
 
+def test_no_library_symbol_left_undefined():
+    # every kernel launch stub and helper of the library is defined in it (a
+    # kernel template whose host stub the compiler dropped shows up here)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", oz.LIB_PATH], capture_output=True, text=True).stdout
+    assert "oz2" not in out, [l for l in out.splitlines() if "oz2" in l][:4]
+
+
 def test_moduli_and_constants_match_oracle():
     assert oz.ozaki2_max_moduli() == 20
     for n in range(2, 21):
