@@ -102,8 +102,13 @@ enum ozaki2_status {
  * C := A * B emulated by Ozaki Scheme II ([Q] steps 1-5). Uses a workspace
  * cached per device, grown on first use of a larger problem (that growth is
  * the only blocking action: hipMalloc after synchronising the device).
- * Calls on one device are serialised by a mutex; use ozaki2_dgemm_ws for
- * concurrent streams.
+ * Every cached-workspace call on a device (ozaki2_dgemm, _sgemm, _zgemm,
+ * _cgemm) shares that one workspace: each call's kernels are made to wait
+ * (hipStreamWaitEvent) for those of the previous such call, whatever stream
+ * it used, so calls on different streams give correct results but run one
+ * after another on the GPU. For products that should overlap, use
+ * ozaki2_dgemm_ws with a workspace per stream. Not capturable into a HIP
+ * graph (it records and waits on a library event); the _ws form is.
  * Returns 0, -1..-11 for an invalid argument (m, n, k, A, lda, B, ldb, C,
  * ldc, num_moduli, mode), OZAKI2_ERR_UNSUPPORTED, OZAKI2_ERR_WORKSPACE or
  * OZAKI2_ERR_HIP. m == 0 or n == 0 returns at once; k == 0 fills C with zeros.
@@ -115,18 +120,28 @@ int ozaki2_dgemm(int64_t m, int64_t n, int64_t k,
 /*
  * Bytes of device workspace ozaki2_dgemm_ws needs for this problem
  * (0 for invalid arguments or empty products). Host-only; no HIP call.
+ * The workspace ([Q] section エミュレーションで足りるかを判断する観点: the
+ * emulation keeps its intermediates in a workspace of its own) holds, for N
+ * moduli, N int8 residue planes of A and of B and N int8 product planes:
+ * about N * (m k + n k + m n) bytes, plus small exponent and norm arrays
+ * (and the bound operands in accurate mode).
  */
 size_t ozaki2_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
 
 /*
  * As ozaki2_dgemm, with a caller-provided DEVICE workspace of at least
- * ozaki2_workspace_size(...) bytes, 256-byte aligned. Never allocates and is
- * re-entrant; calls that share one workspace must be ordered on one stream.
+ * ozaki2_workspace_size(...) bytes, 256-byte aligned (the kernels' 16-byte
+ * vector and 1 KiB LDS-copy accesses rely on it). The workspace holds the
+ * residue planes and products between the steps; [Q] section
+ * エミュレーションで足りるかを判断する観点 notes that such emulation needs a
+ * workspace of its own (gigabytes for large products), which is why the
+ * caller may provide it. Never allocates and is re-entrant; calls that share
+ * one workspace must be ordered on one stream.
  * It only enqueues kernels on the stream (no memset, copy or host
  * synchronisation), so it can be captured into a HIP graph and replayed;
  * timing (ozaki2_timing_enable) must be off while capturing.
- * Returns as ozaki2_dgemm; -12 if workspace is NULL (while needed),
- * OZAKI2_ERR_WORKSPACE if workspace_bytes is too small.
+ * Returns as ozaki2_dgemm; -12 if workspace is NULL (while needed) or not
+ * 256-byte aligned, OZAKI2_ERR_WORKSPACE if workspace_bytes is too small.
  */
 int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k,
                     const double *A, int64_t lda, const double *B, int64_t ldb,
@@ -173,7 +188,7 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k,
  *            bytes.
  * Returns 0; -1 m < 0, -2 n < 0, -3 num_moduli outside [2, 20], -4 residues,
  * -5 e, -6 f or -7 C NULL while needed, -8 ldc < max(1, m), -9 workspace
- * NULL; OZAKI2_ERR_WORKSPACE if workspace_bytes is too small,
+ * NULL or not 256-byte aligned; OZAKI2_ERR_WORKSPACE if workspace_bytes is too small,
  * OZAKI2_ERR_UNSUPPORTED for m or n >= 2^31, OZAKI2_ERR_HIP.
  */
 int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,

@@ -133,10 +133,16 @@ void timing_slots(hipEvent_t **ev, int **tag, bool *all_phases) {
 }
 
 // ---- cached workspace per device ------------------------------------------
+// One workspace per device serves every ozaki2_dgemm/_sgemm/_zgemm/_cgemm call
+// on it, whatever the stream. The mutex orders the host side; on the device,
+// `done` is recorded on the caller's stream after each product's kernels and
+// the next call's stream waits on it first, so products on different streams
+// take the workspace one after another instead of overwriting each other.
 struct Cache {
     std::mutex mu;
     std::vector<void *> ptr;
     std::vector<size_t> bytes;
+    std::vector<hipEvent_t> done;
 };
 Cache g_cache;
 
@@ -250,7 +256,7 @@ int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, in
     }
     const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr, cplx ? 3 : 1);
     if (!use_cache) {
-        if (workspace == nullptr) return -12;
+        if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0) return -12;
         if (wbytes < L.total) return OZAKI2_ERR_WORKSPACE;
         return run(el, cplx, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)workspace, L, dbg, s);
     }
@@ -260,6 +266,13 @@ int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, in
     if ((int)g_cache.ptr.size() <= dev) {
         g_cache.ptr.resize(dev + 1, nullptr);
         g_cache.bytes.resize(dev + 1, 0);
+        g_cache.done.resize(dev + 1, nullptr);
+    }
+    if (g_cache.done[dev] == nullptr) {
+        HIP_TRY(hipEventCreateWithFlags(&g_cache.done[dev], hipEventDisableTiming));
+    } else {
+        // the previous cached product, on whatever stream, is done with the workspace
+        HIP_TRY(hipStreamWaitEvent(s, g_cache.done[dev], 0));
     }
     if (g_cache.bytes[dev] < L.total) {
         if (g_cache.ptr[dev]) {
@@ -273,7 +286,9 @@ int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, in
         g_cache.ptr[dev] = p;
         g_cache.bytes[dev] = L.total;
     }
-    return run(el, cplx, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
+    const int rc = run(el, cplx, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, (char *)g_cache.ptr[dev], L, dbg, s);
+    HIP_TRY(hipEventRecord(g_cache.done[dev], s));
+    return rc;
 }
 
 }  // namespace
@@ -356,7 +371,7 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
     if (C == nullptr && any) return -7;
     if (ldc < (m > 1 ? m : 1)) return -8;
     if (!any) return OZAKI2_SUCCESS;
-    if (workspace == nullptr) return -9;
+    if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0) return -9;
     if (!layout_fits(m, n, 1, OZAKI2_FAST)) return OZAKI2_ERR_UNSUPPORTED;
     const Layout L = make_layout(m, n, 1, num_moduli, OZAKI2_FAST, false);
     if (workspace_bytes < L.total) return OZAKI2_ERR_WORKSPACE;
@@ -509,15 +524,17 @@ void ozaki2_finalize(void) {
         int cur = 0;
         (void)hipGetDevice(&cur);
         for (size_t d = 0; d < g_cache.ptr.size(); ++d) {
-            if (g_cache.ptr[d]) {
+            if (g_cache.ptr[d] || g_cache.done[d]) {
                 (void)hipSetDevice((int)d);
                 (void)hipDeviceSynchronize();
-                (void)hipFree(g_cache.ptr[d]);
+                if (g_cache.ptr[d]) (void)hipFree(g_cache.ptr[d]);
+                if (g_cache.done[d]) (void)hipEventDestroy(g_cache.done[d]);
             }
         }
         (void)hipSetDevice(cur);
         g_cache.ptr.clear();
         g_cache.bytes.clear();
+        g_cache.done.clear();
     }
     std::lock_guard<std::mutex> lk(g_timing.mu);
     timing_free_locked();

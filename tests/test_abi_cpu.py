@@ -119,6 +119,11 @@ def test_workspace_checks():
     need = oz.ozaki2_workspace_size(64, 64, 64, 8, 0)
     assert need > 0
     assert oz.ozaki2_dgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, P, need - 1, 0) == 2
+    # the workspace must be 256-byte aligned (-12, before any HIP call)
+    for off in (8, 16, 128):
+        assert oz.ozaki2_dgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, P + off, need, 0) == -12
+        assert oz.ozaki2_sgemm_ws(64, 64, 64, P, 64, P, 64, P, 64, 8, 0, P + off, need, 0) == -12
+        assert oz.ozaki2_crt_debug(4, 4, 8, P, P, P, P, 4, P + off, 1 << 40, 0) == -9
     assert oz.ozaki2_workspace_size(0, 4, 4, 8, 0) == 0
     assert oz.ozaki2_workspace_size(4, 4, 4, 1, 0) == 0
     # residues dominate: N * (m_pad + n_pad) * k_pad + N * m_pad * n_pad bytes

@@ -54,3 +54,31 @@ def test_concurrent_streams_match_sequential_products():
         torch.cuda.synchronize()
         for i, p in enumerate(prepared):
             assert_bitwise_equal(p["C"].cpu().numpy(), ref[i], f"product {i}, round {rnd}")
+
+
+def test_cached_workspace_calls_on_two_streams():
+    # ozaki2_dgemm (no workspace argument) shares one cached workspace per
+    # device; two different products enqueued back to back on two streams,
+    # without synchronising in between, must each equal the oracle bit for bit
+    # (the library orders their use of the workspace on the device)
+    import oracle as O
+
+    cases = [(1024, 1024, 1024, 14, "fast", 81), (768, 1024, 1024, 16, "accurate", 82)]
+    prepared = []
+    for m, n, k, N, mode, seed in cases:
+        A, B = W.spread_case(m, n, k, 1.0, seed=seed)
+        prepared.append(dict(m=m, n=n, k=k, N=N, md=oz.MODES[mode], dA=device_colmajor(A), dB=device_colmajor(B),
+                             C=torch.empty((n, m), dtype=torch.float64, device="cuda"),
+                             ref=O.os2_dgemm(A, B, N, mode)["C"]))
+    streams = [torch.cuda.Stream() for _ in prepared]
+    for rnd in range(3):
+        for p in prepared:
+            p["C"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        for p, s in zip(prepared, streams):
+            st = oz.ozaki2_dgemm(p["m"], p["n"], p["k"], p["dA"].data_ptr(), p["m"], p["dB"].data_ptr(), p["k"],
+                                 p["C"].data_ptr(), p["m"], p["N"], p["md"], s.cuda_stream)
+            assert st == 0, oz.status_string(st)
+        torch.cuda.synchronize()
+        for i, p in enumerate(prepared):
+            assert_bitwise_equal(p["C"].cpu().numpy().T, p["ref"], f"cached product {i}, round {rnd}")
