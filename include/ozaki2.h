@@ -83,9 +83,11 @@ enum ozaki2_status {
     OZAKI2_SUCCESS = 0,
     OZAKI2_ERR_HIP = 1,         /* a HIP runtime call or kernel launch failed */
     OZAKI2_ERR_WORKSPACE = 2,   /* workspace too small, or its allocation failed */
-    OZAKI2_ERR_UNSUPPORTED = 3  /* size outside the supported range: k > OZAKI2_MAX_K,
+    OZAKI2_ERR_UNSUPPORTED = 3, /* size outside the supported range: k > OZAKI2_MAX_K,
                                    accurate mode with k > OZAKI2_MAX_K_ACCURATE, m or
                                    n >= 2^31, or prod_out requested with k >= 2^17 */
+    OZAKI2_ERR_NOALLOC_LIMIT = 4 /* ozaki2_dgemm_noalloc: the product needs more than
+                                    OZAKI2_NOALLOC_MAX_WORKSPACE bytes of workspace */
 };
 
 #define OZAKI2_MAX_MODULI 20
@@ -147,6 +149,30 @@ int ozaki2_dgemm_ws(int64_t m, int64_t n, int64_t k,
                     const double *A, int64_t lda, const double *B, int64_t ldb,
                     double *C, int64_t ldc, int num_moduli, int mode,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): exactly
+ * ozaki2_dgemm_ws, with the workspace taken from a static device array of
+ * OZAKI2_NOALLOC_MAX_WORKSPACE bytes inside the library instead of an
+ * argument. Each GPU the library is loaded on holds its own copy of that
+ * array until the process ends. The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); on its first call on a device it
+ * looks up the array's device address (hipGetSymbolAddress) and keeps it.
+ * Products whose ozaki2_workspace_size exceeds the array are refused with
+ * OZAKI2_ERR_NOALLOC_LIMIT (about 1024^3 at 20 moduli, 1400^3 at 16 fit).
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (on different streams, or from several threads without ordering
+ * their streams) race and corrupt each other's results: order them on one
+ * stream. The array keeps the last call's contents; nothing in it needs to
+ * start at zero (every call writes all it reads).
+ * Returns as ozaki2_dgemm_ws, with OZAKI2_ERR_NOALLOC_LIMIT in place of the
+ * workspace errors.
+ */
+#define OZAKI2_NOALLOC_MAX_WORKSPACE (128u << 20)
+int ozaki2_dgemm_noalloc(int64_t m, int64_t n, int64_t k,
+                         const double *A, int64_t lda, const double *B, int64_t ldb,
+                         double *C, int64_t ldc, int num_moduli, int mode, void *stream);
 
 /*
  * Test entry point (layout of the copies is stable, timing is not): runs

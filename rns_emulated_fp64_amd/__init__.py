@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libozaki2.so")
 
 FAST = 0
 ACCURATE = 1
+ERR_NOALLOC_LIMIT = 4  # OZAKI2_ERR_NOALLOC_LIMIT
+NOALLOC_MAX_WORKSPACE = 128 << 20  # OZAKI2_NOALLOC_MAX_WORKSPACE
 FAST_ORIGINAL = 2  # comparison stand-in for the original fast-mode rule (see include/ozaki2.h)
 MODES = {"fast": FAST, "accurate": ACCURATE, "original": FAST_ORIGINAL}
 PHASES = ("scale", "split", "gemm", "crt")
@@ -30,7 +32,7 @@ EXPORTS = (
     "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
     "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
     "ozaki2_zgemm", "ozaki2_zgemm_ws", "ozaki2_zgemm_debug", "ozaki2_cgemm", "ozaki2_cgemm_ws", "ozaki2_cgemm_debug",
-    "ozaki2_zgemm_workspace_size",
+    "ozaki2_zgemm_workspace_size", "ozaki2_dgemm_noalloc",
 )
 
 _lib = None
@@ -54,6 +56,8 @@ def lib() -> ctypes.CDLL:
     prod = [i64, i64, i64, p, i64, p, i64, p, i64, i32, i32]
     L.ozaki2_dgemm.argtypes = prod + [p]
     L.ozaki2_dgemm.restype = i32
+    L.ozaki2_dgemm_noalloc.argtypes = prod + [p]
+    L.ozaki2_dgemm_noalloc.restype = i32
     L.ozaki2_workspace_size.argtypes = [i64, i64, i64, i32, i32]
     L.ozaki2_workspace_size.restype = sz
     L.ozaki2_debug_workspace_size.argtypes = [i64, i64, i64, i32, i32]
@@ -93,6 +97,10 @@ def lib() -> ctypes.CDLL:
 # ---- same names as the C ABI: plain integers / device pointers ----------------
 def ozaki2_dgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) -> int:
     return lib().ozaki2_dgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_dgemm_noalloc(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) -> int:
+    return lib().ozaki2_dgemm_noalloc(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
 
 
 def ozaki2_workspace_size(m, n, k, num_moduli, mode) -> int:

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libozaki2.so")
-SOURCES = ["kernels.hip", "api.cpp", "tables.cpp"]
+SOURCES = ["kernels.hip", "api.cpp", "tables.cpp", "noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -292,6 +292,12 @@ int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, in
 }
 
 }  // namespace
+
+int product_ws(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
+               void *C, int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, void *stream) {
+    return front(el, false, m, n, k, A, lda, B, ldb, C, ldc, nmod, mode, workspace, wbytes, false, nullptr, stream);
+}
+
 }  // namespace oz2
 
 using namespace oz2;
@@ -466,6 +472,9 @@ const char *ozaki2_status_string(int status) {
     case OZAKI2_SUCCESS: return "success";
     case OZAKI2_ERR_HIP: return "HIP runtime or kernel launch error";
     case OZAKI2_ERR_WORKSPACE: return "workspace too small or allocation failed";
+    case OZAKI2_ERR_NOALLOC_LIMIT:
+        return "product needs more workspace than the static scratch of ozaki2_dgemm_noalloc "
+               "(OZAKI2_NOALLOC_MAX_WORKSPACE bytes); use ozaki2_dgemm_ws";
     case OZAKI2_ERR_UNSUPPORTED:
         return "unsupported size (k <= 2^22 - 1, or 2^19 - 1 in accurate mode; m, n < 2^31; raw products need k < 2^17)";
     default: break;

@@ -1,5 +1,5 @@
-// common.h -- declarations shared by the host API (api.cpp) and the HIP
-// kernels (kernels.hip) of libozaki2.
+// common.h -- declarations shared by the host API (api.cpp, noalloc.hip) and
+// the HIP kernels (kernels.hip) of libozaki2.
 //
 // Ozaki Scheme II steps follow the Qiita article "8ビットの整数で53ビットの倍精度
 // を組み立てる。中国剰余定理をGPUに載せたOzaki Scheme II" ([Q]) and the summary
@@ -86,6 +86,12 @@ struct Ev {
 
 // Element type of A, B and C: FP64 (ozaki2_dgemm) or binary32 (ozaki2_sgemm).
 enum class Elem { f64, f32 };
+
+// A real product on a caller-provided workspace: the checks and phases of
+// ozaki2_dgemm_ws / ozaki2_sgemm_ws (api.cpp), for the library's other entry
+// points. Returns an ozaki2 status.
+int product_ws(Elem el, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
+               void *C, int64_t ldc, int nmod, int mode, void *workspace, size_t wbytes, void *stream);
 
 // ---- kernel launchers (kernels.hip). Each returns hipGetLastError(). ----
 // cplx: interleaved complex operands (A, B, C hold (re, im) pairs; leading

@@ -44,6 +44,19 @@ def test_no_library_symbol_left_undefined():
     assert "oz2" not in out, [l for l in out.splitlines() if "oz2" in l][:4]
 
 
+def test_noalloc_host_checks():
+    # argument errors and the array limit come back before any HIP call
+    assert oz.ozaki2_dgemm_noalloc(-1, 4, 4, P, 4, P, 4, P, 4, 8, 0, 0) == -1
+    assert oz.ozaki2_dgemm_noalloc(4, 4, 4, P, 4, P, 4, P, 4, 1, 0, 0) == -10
+    assert oz.ozaki2_dgemm_noalloc(0, 4, 4, P, 1, P, 4, P, 1, 8, 0, 0) == 0
+    assert oz.ozaki2_dgemm_noalloc(4096, 4096, 4096, P, 4096, P, 4096, P, 4096, 16, 0, 0) == oz.ERR_NOALLOC_LIMIT
+    assert "noalloc" in oz.status_string(oz.ERR_NOALLOC_LIMIT)
+    # the header's limit is the binding's
+    text = open(HEADER).read()
+    assert "#define OZAKI2_NOALLOC_MAX_WORKSPACE (128u << 20)" in text
+    assert oz.NOALLOC_MAX_WORKSPACE == 128 << 20
+
+
 def test_moduli_and_constants_match_oracle():
     assert oz.ozaki2_max_moduli() == 20
     for n in range(2, 21):
