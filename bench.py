@@ -7,9 +7,11 @@ int8 operations per launch over its average launch time, from HIP events on
 the library's stream in the timed region, against the 5000 TOP/s dense INT8
 peak; ``traffic`` is its HBM bytes per launch from the committed counter
 record while the GEMM source still matches it. ``cpu_baseline`` times the CPU
-oracle on a bounded row sample of the same workload. The default 40 warm-up
-steps put the timed region past the clock transient that follows a cold start
-(the first GEMMs after idle run up to 1.4x slower for about 25 ms).
+oracle on the same workload (all rows of A up to 4096^3, else a bounded row
+sample). Warm-up runs at least --warmup steps and at least 100 ms, which puts
+the timed region past the clock transient that follows a cold start (the
+first GEMMs after idle run up to 1.4x slower for about 25 ms), whatever
+--warmup says.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
                        [--mode fast|accurate] [--no-cpu-baseline]
@@ -88,6 +90,75 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def host_info():
+    """CPU model and core counts of the host this runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        usable = os.cpu_count()
+    return dict(cpu_model=model, nproc=usable, cpu_count=os.cpu_count())
+
+
+def _sclk_files():
+    """sysfs files listing the GPU core clock levels (the current one starred)."""
+    import glob
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def _read_sclk(path):
+    """Current core clock in MHz from a pp_dpm_sclk listing, or None."""
+    try:
+        with open(path) as fh:
+            for line in fh:
+                if "*" in line:
+                    tok = line.split(":", 1)[1].strip().split()[0].lower()
+                    return int(float(tok.replace("mhz", "")))
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def sample_clocks(step, torch, samples=40, every_steps=4):
+    """Core clock readings (MHz) from sysfs while the product runs in a loop,
+    after the timed region so the timed steps are untouched; reported as
+    min / median / max of the samples, or None where sysfs has no listing."""
+    files = _sclk_files()
+    if not files:
+        return None
+    vals = []
+    for _ in range(samples):
+        for _ in range(every_steps):
+            step()
+        v = _read_sclk(files[0])
+        if v is not None:
+            vals.append(v)
+    torch.cuda.synchronize()
+    if not vals:
+        return None
+    vals.sort()
+    return dict(source=files[0].replace("/sys/class/drm/", ""), samples=len(vals), min_mhz=vals[0],
+                median_mhz=vals[len(vals) // 2], max_mhz=vals[-1])
+
+
+def phase_bytes(m, n, k, N, elem, cplx):
+    """Algorithmic HBM bytes of each phase: operands read, residue planes
+    written and read once (int8), C written; no padding, no re-reads."""
+    planes = 3 * N if cplx else N
+    ops = elem * (m * k + k * n)
+    res = planes * (m * k + n * k)
+    prod = planes * m * n
+    return dict(scale=ops, split=ops + res, gemm=res + prod, crt=prod + elem * m * n)
+
+
 def time_steps(fn, steps, warmup, torch, settle_ms=60.0):
     """Mean ms per call of fn over `steps` calls, after at least `warmup`
     calls and at least `settle_ms` of warm-up (the clock settles under load)."""
@@ -104,8 +175,9 @@ def time_steps(fn, steps, warmup, torch, settle_ms=60.0):
     return (time.perf_counter() - t0) * 1e3 / steps
 
 
-def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
-    """The oracle (as it stands) on a bounded sample: the first rows of A times all of B."""
+def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted, gpu_e=None, gpu_f=None):
+    """The oracle (as it stands) on the first rows of A times all of B: every
+    row up to 4096^3 work, else a bounded sample of about that size."""
     import numpy as np
     import oracle as O
     try:
@@ -116,7 +188,7 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
     omp_threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     m, k = A.shape
     n = B.shape[1]
-    rows = rows_wanted or max(8, min(m, int(3072 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
+    rows = rows_wanted or max(8, min(m, int(4096 * (4096 / max(k, 1)) * (4096 / max(n, 1)))))
     rows = min(rows, m)
     single = A.dtype == np.float32
     emul = O.os2_sgemm if single else O.os2_dgemm
@@ -138,10 +210,21 @@ def cpu_baseline_leg(A, B, C_gpu, N, mode, rows_wanted):
     t0 = time.perf_counter()
     _ = A[:rows] @ B
     t_host = time.perf_counter() - t0
+    # exponents: GPU against the oracle on the same rows and all columns
+    # (a mismatch is allowed only at a rounding boundary; expected 0)
+    exp_mm = None
+    if gpu_e is not None and gpu_f is not None:
+        as_int = lambda v: [(-(2 ** 31) if x is None else int(x)) for x in v]
+        exp_mm = int(sum(a != b for a, b in zip(as_int(r["e"]), gpu_e[:rows]))) + \
+            int(sum(a != b for a, b in zip(as_int(r["f"]), gpu_f)))
+    hi_ = host_info()
     return dict(value=value, unit="TFLOPS", cores=max(omp_threads, blas_threads), kind="oracle",
-                sample=f"rows 0..{rows - 1} of A times all of B ({rows}x{n}x{k}, N={N}, {mode}); "
-                       f"{t:.2f} s; OpenMP {omp_threads} threads, BLAS {blas_threads} threads"), \
-        dict(parity_mismatches=int(diff.sum()), parity_entries=int(Cs.size), error_rows=er, **err,
+                sample=(f"all {rows} rows of A times all of B" if rows == m else
+                        f"rows 0..{rows - 1} of A times all of B") + f" ({rows}x{n}x{k}, N={N}, {mode}); "
+                       f"{t:.2f} s; OpenMP {omp_threads} threads, BLAS {blas_threads} threads",
+                **hi_), \
+        dict(parity_mismatches=int(diff.sum()), parity_entries=int(Cs.size), exponent_mismatches=exp_mm,
+             exponents_compared=(rows + n) if exp_mm is not None else 0, error_rows=er, **err,
              **{f"native_{nat}_E_cw": native["E_cw"], f"native_{nat}_E_el": native["E_el"],
                 f"host_native_{nat}_gemm_tflops": round(2.0 * rows * n * k / t_host / 1e12, 4)})
 
@@ -296,11 +379,19 @@ def main():
         if st:
             raise RuntimeError(oz.status_string(st))
 
-    # timed region: K steps, per-phase HIP events recorded on the same stream
-    for _ in range(args.warmup):
+    # warm-up: at least --warmup steps and at least 100 ms of steps, so the
+    # timed region starts after the clock transient of a cold start
+    settle_ms = 100.0
+    t0 = time.perf_counter()
+    warm = 0
+    while warm < args.warmup or (time.perf_counter() - t0) * 1e3 < settle_ms:
         step()
+        warm += 1
+        if warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # timed region: HIP events around the GEMM of every step (same stream)
+    warmup_ms = (time.perf_counter() - t0) * 1e3
+    # timed region: HIP events attached to the GEMM launch of every step (same stream)
     oz.ozaki2_timing_enable(args.steps, all_phases=False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -308,8 +399,10 @@ def main():
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    gemm_ms, calls = oz.ozaki2_timing_read()
-    gemm_avg = gemm_ms["gemm"] / max(calls, 1)
+    per_call = sorted(c["gemm"] for c in oz.ozaki2_timing_read_calls(args.steps))
+    gemm_avg = sum(per_call) / max(len(per_call), 1)
+    gemm_min = per_call[0] if per_call else 0.0
+    gemm_med = per_call[len(per_call) // 2] if per_call else 0.0
     # per-phase breakdown from a separate, untimed pass
     nb = max(3, min(args.steps, 10))
     oz.ozaki2_timing_enable(nb, all_phases=True)
@@ -319,6 +412,10 @@ def main():
     oz.ozaki2_timing_enable(0)
     phase_avg = {p: v / max(pcalls, 1) for p, v in phase_ms.items()}
     log(f"{ms:.3f} ms/step; GEMM {gemm_avg:.4f} ms (timed region); phases {phase_avg}")
+    elem = (16 if not single else 8) if cplx else (4 if single else 8)
+    pbytes = phase_bytes(m, n, k, N, elem, cplx)
+    phase_gbs = {p: round(pbytes[p] / (phase_avg[p] * 1e-3) / 1e9, 1) for p in pbytes if phase_avg.get(p, 0) > 0}
+    clocks = None if args.no_extras else sample_clocks(step, torch)
 
     flops = (8.0 if cplx else 2.0) * m * n * k  # a complex multiply-add is 8 real flops
     tflops = flops / (ms * 1e-3) / 1e12
@@ -417,7 +514,20 @@ def main():
     cpu = None
     accuracy = None
     if not args.no_cpu_baseline and not cplx:
-        cpu, accuracy = cpu_baseline_leg(A, B, C, N, args.mode, args.cpu_rows)
+        # the GPU's exponents of this product (debug entry point, e and f only)
+        dbg_wb = oz.ozaki2_debug_workspace_size(m, n, k, N, md)
+        dbg_ws = torch.empty(dbg_wb, dtype=torch.uint8, device=dev)
+        e_dev = torch.empty(max(m, 1), dtype=torch.int32, device=dev)
+        f_dev = torch.empty(max(n, 1), dtype=torch.int32, device=dev)
+        dbg = oz.ozaki2_sgemm_debug if single else oz.ozaki2_dgemm_debug
+        st = dbg(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, md, dbg_ws.data_ptr(), dbg_wb,
+                 e_dev.data_ptr(), f_dev.data_ptr(), None, None, None, None, stream)
+        if st:
+            raise RuntimeError(oz.status_string(st))
+        torch.cuda.synchronize()
+        gpu_e, gpu_f = e_dev[:m].cpu().tolist(), f_dev[:n].cpu().tolist()
+        del dbg_ws
+        cpu, accuracy = cpu_baseline_leg(A, B, C, N, args.mode, args.cpu_rows, gpu_e, gpu_f)
     elif not args.no_cpu_baseline:
         cpu, accuracy = cpu_baseline_complex(A, B, C, N, args.cpu_rows)
 
@@ -433,7 +543,14 @@ def main():
         emulated_vs_fp64_peak=round(tflops / FP64_PEAK_TFLOPS, 3),
         gemm_int8_peak_frac=roofline["frac"],
         gemm_ms_timed_region=round(gemm_avg, 4),
+        gemm_ms_timed_min=round(gemm_min, 4),
+        gemm_ms_timed_median=round(gemm_med, 4),
+        warmup_steps_run=warm,
+        warmup_ms=round(warmup_ms, 1),
         phase_ms={p: round(v, 4) for p, v in phase_avg.items()},
+        phase_gbs=phase_gbs,
+        phase_bytes=pbytes,
+        gpu_clocks=clocks,
         roofline=roofline,
         cpu_baseline=cpu,
         accuracy=accuracy,

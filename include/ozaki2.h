@@ -347,6 +347,13 @@ const char *ozaki2_status_string(int status);
  */
 int ozaki2_timing_enable(int max_calls, int all_phases);
 int ozaki2_timing_read(double *ms_out, int *calls);
+/*
+ * As ozaki2_timing_read, per call: writes the milliseconds of phase p of
+ * timed call c to HOST ms_out[c * 4 + p] (ms_out may be NULL to discard) and
+ * clears the record. Returns 0, -2 if max_calls is below the number of timed
+ * calls (nothing cleared), or OZAKI2_ERR_HIP.
+ */
+int ozaki2_timing_read_calls(double *ms_out, int max_calls, int *calls);
 
 /* Frees the cached workspaces, timing events and tables. */
 void ozaki2_finalize(void);

@@ -30,6 +30,7 @@ EXPORTS = (
     "ozaki2_dgemm", "ozaki2_workspace_size", "ozaki2_dgemm_ws", "ozaki2_dgemm_debug",
     "ozaki2_debug_workspace_size", "ozaki2_max_moduli", "ozaki2_moduli", "ozaki2_scaling_constant",
     "ozaki2_crt_weight", "ozaki2_status_string", "ozaki2_timing_enable", "ozaki2_timing_read",
+    "ozaki2_timing_read_calls",
     "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
     "ozaki2_zgemm", "ozaki2_zgemm_ws", "ozaki2_zgemm_debug", "ozaki2_cgemm", "ozaki2_cgemm_ws", "ozaki2_cgemm_debug",
     "ozaki2_zgemm_workspace_size", "ozaki2_dgemm_noalloc",
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_timing_enable.restype = i32
     L.ozaki2_timing_read.argtypes = [p, p]
     L.ozaki2_timing_read.restype = i32
+    L.ozaki2_timing_read_calls.argtypes = [p, i32, p]
+    L.ozaki2_timing_read_calls.restype = i32
     L.ozaki2_finalize.argtypes = []
     L.ozaki2_finalize.restype = None
     _lib = L
@@ -220,6 +223,16 @@ def ozaki2_timing_read() -> tuple[dict, int]:
     if st:
         raise Ozaki2Error(st, "ozaki2_timing_read")
     return dict(zip(PHASES, list(ms))), calls.value
+
+
+def ozaki2_timing_read_calls(max_calls: int) -> list:
+    """Per timed call, a dict of milliseconds per phase; clears the record."""
+    ms = (ctypes.c_double * (4 * max(max_calls, 1)))()
+    calls = ctypes.c_int()
+    st = lib().ozaki2_timing_read_calls(ms, max_calls, ctypes.byref(calls))
+    if st:
+        raise Ozaki2Error(st, "ozaki2_timing_read_calls")
+    return [dict(zip(PHASES, list(ms[4 * c:4 * c + 4]))) for c in range(calls.value)]
 
 
 def ozaki2_finalize() -> None:

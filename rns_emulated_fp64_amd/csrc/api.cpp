@@ -505,12 +505,14 @@ int ozaki2_timing_enable(int max_calls, int all_phases) {
     return OZAKI2_SUCCESS;
 }
 
-int ozaki2_timing_read(double *ms_out, int *calls) {
+int ozaki2_timing_read_calls(double *ms_out, int max_calls, int *calls) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
-    double acc[kNumPhases] = {0, 0, 0, 0};
-    for (int c = 0; c < g_timing.used; ++c) {
+    const int used = g_timing.used;
+    if (ms_out && max_calls < used) return -2;
+    for (int c = 0; c < used; ++c) {
         hipEvent_t *ev = &g_timing.ev[(size_t)c * (2 * kMaxIntervals)];
         int *tag = &g_timing.tag[(size_t)c * kMaxIntervals];
+        double acc[kNumPhases] = {0, 0, 0, 0};
         for (int t = 0; t < kMaxIntervals; ++t) {
             if (tag[t] < 0) continue;
             if (hipEventSynchronize(ev[2 * t + 1]) != hipSuccess) return OZAKI2_ERR_HIP;
@@ -519,11 +521,31 @@ int ozaki2_timing_read(double *ms_out, int *calls) {
             acc[tag[t]] += ms;
             tag[t] = -1;
         }
+        if (ms_out)
+            for (int p = 0; p < kNumPhases; ++p) ms_out[(size_t)c * kNumPhases + p] = acc[p];
     }
-    if (ms_out)
-        for (int p = 0; p < kNumPhases; ++p) ms_out[p] = acc[p];
-    if (calls) *calls = g_timing.used;
+    if (calls) *calls = used;
     g_timing.used = 0;
+    return OZAKI2_SUCCESS;
+}
+
+int ozaki2_timing_read(double *ms_out, int *calls) {
+    int used = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_timing.mu);
+        used = g_timing.used;
+    }
+    std::vector<double> per((size_t)(used > 0 ? used : 1) * kNumPhases, 0.0);
+    const int st = ozaki2_timing_read_calls(per.data(), used, &used);
+    if (st != OZAKI2_SUCCESS) return st;
+    if (ms_out) {
+        for (int p = 0; p < kNumPhases; ++p) {
+            double sum = 0.0;
+            for (int c = 0; c < used; ++c) sum += per[(size_t)c * kNumPhases + p];
+            ms_out[p] = sum;
+        }
+    }
+    if (calls) *calls = used;
     return OZAKI2_SUCCESS;
 }
 

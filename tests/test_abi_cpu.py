@@ -178,6 +178,7 @@ def test_timing_off_and_empty_read_need_no_device():
     oz.ozaki2_timing_enable(0)
     ms, calls = oz.ozaki2_timing_read()
     assert calls == 0 and ms == {p: 0.0 for p in oz.PHASES}
+    assert oz.ozaki2_timing_read_calls(0) == []
 
 
 def test_bench_refuses_more_than_one_gpu():

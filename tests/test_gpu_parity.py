@@ -16,7 +16,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_util import assert_bitwise_equal, full_parity, run_debug, run_ws, stream_handle, device_colmajor
+from gpu_util import (assert_bitwise_equal, full_parity, reconcile_exponents, run_debug, run_ws, stream_handle,
+                      device_colmajor)
 import rns_emulated_fp64_amd as oz
 
 pytestmark = pytest.mark.gpu
@@ -192,39 +193,18 @@ def _sampled_exact_check(A, B, C, e, f, rows, cols):
 
 @pytest.mark.parametrize("mode", ["fast", "accurate"])
 def test_config_spread1_4096_n16(mode):
-    # The headline workload at full size, in the configuration the benchmark times.
+    # The headline workload at full size, in the launch configuration the
+    # benchmark times: every exponent (mismatch protocol), every int8 residue
+    # of A and B, every int32 residue product, every reduced residue and every
+    # entry of C against the oracle's os2_dgemm, bit for bit.
     A, B = W.make("spread1.0_4096_n16")
     N = 16
-    g = run_debug(A, B, N, mode, want_prod=False)
-    e = g["e"].tolist()
-    f = g["f"].tolist()
-    rng = np.random.default_rng(1)
-    rows = np.sort(rng.choice(4096, 24, replace=False)).tolist()
-    cols = np.sort(rng.choice(4096, 24, replace=False)).tolist()
-    # exponents of the sampled rows/columns against the oracle (protocol on mismatch)
-    Pp = O.scaling_constant(math.prod(O.choose_moduli(N)))
-    if mode == "fast":
-        oe = O.fast_exponents_rows(A[rows], Pp)
-        of = O.fast_exponents_rows(B[:, cols].T, Pp)
-        assert sum(a != b for a, b in zip(oe, [e[i] for i in rows])) <= 1
-        assert sum(a != b for a, b in zip(of, [f[j] for j in cols])) <= 1
-    else:
-        oe, of = O.exponents(A, B, N, "accurate")
-        assert oe == e and of == f
-    # residues of sampled rows, bit-exact
-    mods = O.choose_moduli(N)
-    assert np.array_equal(g["RA"][:, rows, :], O.split(A[rows], [e[i] for i in rows], mods))
-    assert np.array_equal(g["RB"][:, cols, :], O.split(B[:, cols].T, [f[j] for j in cols], mods))
-    # reduced products on sampled entries
-    RA = g["RA"][:, rows, :].astype(np.int64)
-    RB = g["RB"][:, cols, :].astype(np.int64)
-    for l, p in enumerate(mods):
-        Q = RA[l] @ RB[l].T
-        assert np.array_equal(np.mod(Q, p), g["red"][l][np.ix_(cols, rows)].T)
-    # C bit-exact on sampled entries, and the launch configuration of the benchmark agrees
-    _sampled_exact_check(A, B, g["C"], e, f, rows, cols)
+    g, r, mismatches = full_parity(A, B, N, mode, want_prod=True)
+    print(f"4096^3 N=16 {mode}: exponent mismatches {mismatches}")
     C_ws = run_ws(A, B, N, mode)
     assert_bitwise_equal(C_ws, g["C"], "ws vs debug")
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(4096, 24, replace=False)).tolist()
     hi, lo = O.dd_gemm(A[rows], B)
     err = O.error_metrics(g["C"][rows], hi, lo, A[rows], B)
     print(f"4096^3 N=16 {mode}:", err)
@@ -274,12 +254,17 @@ def test_scale_sweep_original_rule_stand_in():
 
 def test_config_spread1_16384_n18():
     # 16384^3, N = 18 (2 GiB per operand; |x| reaches 2^69.7, beyond int64):
-    # exponents of sampled rows/columns, C bit-exact on sampled entries, and the
-    # accuracy gate on sampled rows.
+    # every column exponent of B and the sampled rows' exponents of A (mismatch
+    # protocol), the int8 residues of the sampled rows of A and columns of B,
+    # and whole sampled rows of C bit for bit against os2_dgemm(A[rows], B),
+    # plus the accuracy gate on three of them.
     A, B = W.make("spread1.0_16384_n18")
     m, k = A.shape
     n = B.shape[1]
     N = 18
+    rng = np.random.default_rng(3)
+    rows = np.sort(rng.choice(m, 6, replace=False)).tolist()
+    cols = np.sort(rng.choice(n, 6, replace=False)).tolist()
     dA = device_colmajor(A)
     dB = device_colmajor(B)
     dC = torch.empty((n, m), dtype=torch.float64, device="cuda")
@@ -287,31 +272,33 @@ def test_config_spread1_16384_n18():
     ws = torch.empty(wbytes, dtype=torch.uint8, device="cuda")
     e = torch.empty(m, dtype=torch.int32, device="cuda")
     f = torch.empty(n, dtype=torch.int32, device="cuda")
+    ra = torch.empty((N, m, k), dtype=torch.int8, device="cuda")
+    rb = torch.empty((N, n, k), dtype=torch.int8, device="cuda")
     st = oz.ozaki2_dgemm_debug(m, n, k, dA.data_ptr(), m, dB.data_ptr(), k, dC.data_ptr(), m, N, 0, ws.data_ptr(),
-                               wbytes, e.data_ptr(), f.data_ptr(), None, None, None, None, stream_handle())
+                               wbytes, e.data_ptr(), f.data_ptr(), ra.data_ptr(), rb.data_ptr(), None, None,
+                               stream_handle())
     assert st == 0
     torch.cuda.synchronize()
     del ws, dA, dB
-    rng = np.random.default_rng(3)
-    rows = np.sort(rng.choice(m, 6, replace=False)).tolist()
-    cols = np.sort(rng.choice(n, 6, replace=False)).tolist()
-    C = dC[cols, :][:, rows].cpu().numpy().T  # C[rows][:, cols]
-    Crows = dC[:, rows[:3]].cpu().numpy().T   # full rows for the accuracy gate
-    ge = e.cpu().numpy().tolist()
-    gf = f.cpu().numpy().tolist()
-    Pp = O.scaling_constant(math.prod(O.choose_moduli(N)))
-    oe = O.fast_exponents_rows(A[rows], Pp)
-    of = O.fast_exponents_rows(B[:, cols].T, Pp)
-    assert sum(a != b for a, b in zip(oe, [ge[i] for i in rows])) == 0
-    assert sum(a != b for a, b in zip(of, [gf[j] for j in cols])) == 0
-    Ai = O.scaled_integers(A[rows], [ge[i] for i in rows])
-    Bi = O.scaled_integers(B[:, cols].T, [gf[j] for j in cols])
-    Y = Ai.dot(Bi.T)
+    RA_s = ra[:, rows, :].cpu().numpy()
+    RB_s = rb[:, cols, :].cpu().numpy()
+    del ra, rb
+    C_rows = dC[:, rows].cpu().numpy().T  # whole rows of C
+    ge = e.cpu().numpy()
+    gf = f.cpu().numpy()
+    del dC
+    r = O.os2_dgemm(A[rows], B, N)
+    er, ne = reconcile_exponents(ge[rows], r["e"], A[rows], N, "fast")
+    ef, nf = reconcile_exponents(gf, r["f"], B.T, N, "fast")
+    if ne or nf:
+        r = O.os2_dgemm(A[rows], B, N, e=er, f=ef)
+    print(f"16384^3 N=18: exponent mismatches {ne + nf} of {len(rows) + n}")
+    assert np.array_equal(RA_s, r["RA"]), "residues of the sampled rows of A differ"
+    assert np.array_equal(RB_s, r["RB"][:, cols, :]), "residues of the sampled columns of B differ"
+    assert_bitwise_equal(C_rows, r["C"], "sampled rows of C at 16384^3")
     P = math.prod(O.choose_moduli(N))
-    assert np.all(2 * np.abs(Y) <= P - 1)
-    ref = O.unscale(Y, [ge[i] for i in rows], [gf[j] for j in cols])
-    assert_bitwise_equal(C, ref, "sampled C at 16384^3")
+    assert np.all(2 * np.abs(r["X"]) <= P - 1)
     hi, lo = O.dd_gemm(A[rows[:3]], B)
-    err = O.error_metrics(Crows, hi, lo, A[rows[:3]], B)
+    err = O.error_metrics(C_rows[:3], hi, lo, A[rows[:3]], B)
     print("16384^3 N=18:", err)
     assert err["E_cw"] <= 1e-14

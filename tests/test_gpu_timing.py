@@ -62,6 +62,16 @@ def test_timing_changes_no_bit_and_reports_phases(mode):
     ms, calls = oz.ozaki2_timing_read()
     assert calls == 0 and all(v == 0.0 for v in ms.values())
 
+    # per call: one dict per timed call, summing to what the total read gives
+    oz.ozaki2_timing_enable(3, all_phases=True)
+    outs += [run(), run()]
+    with pytest.raises(oz.Ozaki2Error):
+        oz.ozaki2_timing_read_calls(1)  # too small: nothing cleared
+    per = oz.ozaki2_timing_read_calls(3)
+    assert len(per) == 2
+    assert all(0.0 < c[p] < 1000.0 for c in per for p in oz.PHASES), per
+    assert oz.ozaki2_timing_read_calls(3) == []
+
     # calls beyond the events created run untimed
     oz.ozaki2_timing_enable(1)
     outs += [run() for _ in range(3)]
