@@ -39,7 +39,13 @@
  *
  * Environment: OZ2_GEMM_TILE=128 or 256 forces the INT8 GEMM's block shape
  * (by default 256 x 256, or 128 x 128 for products too small to give every
- * two compute units a 256 x 256 block); results do not depend on it.
+ * two compute units a 256 x 256 block); OZ2_FUSED=1 runs steps 3-5 of real
+ * products as one launch (every modulus of a 64 x 64 tile of C in one block,
+ * reconstructed in registers; [Q] section 誤差のないINT8行列積(手順3): the
+ * per-modulus products are independent), OZ2_FUSED=0 as two (the default
+ * form, a 256 x 256 GEMM writing residue planes and a reconstruction reading
+ * them); the debug entry points always use two. Results do not depend on
+ * either setting.
  *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by

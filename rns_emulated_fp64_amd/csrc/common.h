@@ -116,6 +116,12 @@ hipError_t launch_accurate_exponents(int64_t m, int64_t n, double Pp, const Layo
                                      hipStream_t s, Ev ev = {});
 hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,
                       const CrtConsts &cc, void *C, int64_t ldc, const Layout &L, hipStream_t s, Ev ev = {});
+// Steps 3-5 in one launch (real products): all moduli of a 64 x 64 tile of C
+// per block, reconstructed in registers; applies when gemm_crt_applies.
+bool gemm_crt_applies(const Layout &L, int64_t m, int64_t n);
+hipError_t launch_gemm_crt(Elem el, const int8_t *RA, const int8_t *RB, int64_t m, int64_t n, const int32_t *e,
+                           const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
+                           const Layout &L, hipStream_t s, Ev ev = {});
 hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e,
                               const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
                               const Layout &L, hipStream_t s, Ev ev = {});

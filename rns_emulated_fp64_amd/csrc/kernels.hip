@@ -1362,6 +1362,150 @@ __global__ __launch_bounds__(256) void k_crt_c(const int8_t *__restrict__ planes
 }
 
 // ---------------------------------------------------------------------------
+// Steps 3 + 4 + 5 fused: all moduli of one output tile in one block
+// ---------------------------------------------------------------------------
+// The per-modulus products are independent and carry nothing from one clock
+// to another ([Q] section 誤差のないINT8行列積(手順3)), so one block may run them
+// back to back for its tile: after the inner dimension of modulus l it reduces
+// the int32 products mod p_l in registers and adds c_l W_l into the tile's
+// exact 40-bit pieces S (as k_crt does from the planes); after the last
+// modulus it lifts, unscales and writes C ([Q] sections 高い精度での復元(手順4)
+// and 2の累乗による整数化(手順1と5)). No residue plane leaves the chip and the
+// reconstruction needs no launch of its own. The price is a small tile: the N
+// residues or the pieces S of a 256 x 256 tile fit neither the registers nor
+// LDS, while a 64 x 64 tile keeps S in 128 VGPRs per lane; so each MFMA needs
+// 1 KiB of LDS fragments (0.375 KiB in the 256 x 256 GEMM), the L2 serves four
+// times the operand bytes per operation, and the block count no longer grows
+// with the number of moduli.
+//
+// Block: 4 waves (2 x 2) of 32 x 32 (2 x 2 MFMA tiles of 16 x 16 x 64); LDS
+// ring of kFNST stages of 8 KiB (4 A and 4 B fragment blocks of 64 k), one
+// continuous sequence of stages over (modulus, k) so the copies of the next
+// modulus start during the last stages of the current one. Each wave copies 2
+// fragment blocks per stage (waves 0, 1: A; waves 2, 3: B).
+constexpr int kFTile = 64;
+constexpr int kFNST = 4;
+constexpr int kFStage = 8 * 1024;
+
+template <class OutT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_crt(
+    const int8_t *__restrict__ RA, const int8_t *__restrict__ RB, int64_t planeA, int64_t planeB, int nk,
+    int tiles_m, const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, ModConsts mc,
+    OutT *__restrict__ C, int64_t m, int64_t n, int64_t ldc) {
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kFNST * kFStage];
+    const int tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t row_bytes = (int64_t)nk * 1024;  // one 16-row block over all of K
+    const bool copies_a = wave < 2;
+    const int cq = (wave & 1) * 2;
+    const int8_t *base = (copies_a ? RA + ((int64_t)tm * 4 + cq) * row_bytes : RB + ((int64_t)tn * 4 + cq) * row_bytes) +
+                         lane * 16;
+    const int64_t plane = copies_a ? planeA : planeB;
+    const int total = cc.n * nk;  // stages over all moduli (even: nk is even)
+    __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
+    // copies of global stage g = l * nk + ks (clamped past the end: into a slot never read)
+    int cl = 0, cks = 0;  // (modulus, k-stage) of the next stage to copy
+    auto copy_next = [&](int g) {
+        const int8_t *src = base + cl * plane + cks * 1024;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            __builtin_amdgcn_global_load_lds(src + q * row_bytes, lds3 + (g % kFNST) * kFStage + (wave * 2 + q) * 1024,
+                                             16, 0, 0);
+        if (g + 1 < total) {
+            if (++cks == nk) {
+                cks = 0;
+                ++cl;
+            }
+        }
+    };
+    // fragment r of a stage: r < 2 -> A tile r of this wave, else B tile r - 2
+    auto frag = [&](const int8_t *stage, int r) {
+        return *(const v4i *)(stage + (r < 2 ? 2 * wm + r : 4 + 2 * wn + (r - 2)) * 1024 + lane * 16);
+    };
+
+    v4i acc[2][2];
+    double S[2][2][4][4];  // [row tile][col tile][register][piece]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            acc[i][j] = (v4i){0, 0, 0, 0};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) S[i][j][v][t] = 0.0;
+        }
+
+#pragma unroll
+    for (int g = 0; g < kFNST - 1; ++g) copy_next(g);
+    asm volatile("s_waitcnt vmcnt(2)\n\ts_barrier" ::: "memory");  // stages 0 and 1 landed
+    v4i f0[4], f1[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f0[r] = frag(lds, r);
+
+    int l = 0, ks = 0;  // modulus and k-stage of the stage being multiplied
+    // stage g: MFMAs on fc, reads of stage g + 1 into fn, copies of stage g + 3;
+    // at the end stage g + 2 has landed and every read of stage g + 1's slot is
+    // done before the copies of a later stage refill it
+    auto stage = [&](int g, v4i(&fc)[4], v4i(&fn)[4]) {
+        const int8_t *nxt = lds + ((g + 1) % kFNST) * kFStage;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[q >> 1][q & 1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q >> 1], fc[2 + (q & 1)], acc[q >> 1][q & 1], 0, 0, 0);
+            fn[q] = frag(nxt, q);
+        }
+        copy_next(g + kFNST - 1);
+        asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        if (++ks == nk) {
+            // modulus l done: its residues, weighted, into the pieces S
+            const double p = mc.p[l], pinv = mc.pinv[l];
+            const double w0 = cc.w[l][0], w1 = cc.w[l][1], w2 = cc.w[l][2], w3 = cc.w[l][3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const double c = (double)smod(acc[i][j][v], pinv, (int)p);
+                        S[i][j][v][0] = fma(c, w0, S[i][j][v][0]);
+                        S[i][j][v][1] = fma(c, w1, S[i][j][v][1]);
+                        S[i][j][v][2] = fma(c, w2, S[i][j][v][2]);
+                        S[i][j][v][3] = fma(c, w3, S[i][j][v][3]);
+                    }
+                    acc[i][j] = (v4i){0, 0, 0, 0};
+                }
+            ks = 0;
+            ++l;
+        }
+    };
+    for (int g = 0; g < total; g += 2) {
+        stage(g, f0, f1);
+        stage(g + 1, f1, f0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
+
+    // accumulator layout of a 16 x 16 tile: lane L, register v holds row
+    // 4 (L / 16) + v, column L % 16
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t col = (int64_t)tn * kFTile + wn * 32 + 16 * j + (lane & 15);
+        if (col >= n) continue;
+        const int fj = f[col];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t row0 = (int64_t)tm * kFTile + wm * 32 + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = row0 + v;
+                if (row < m) C[row + col * ldc] = crt_finish<OutT>(S[i][j][v], e[row], fj, cc);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small helpers
 // ---------------------------------------------------------------------------
 template <class T>
@@ -1633,6 +1777,30 @@ static hipError_t launch_crt_t(const int8_t *planes, int64_t m, int64_t n, const
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     }
     return hipGetLastError();
+}
+
+template <class OutT>
+static hipError_t launch_gemm_crt_t(const int8_t *RA, const int8_t *RB, int64_t m, int64_t n, const int32_t *e,
+                                   const int32_t *f, const CrtConsts &cc, const ModConsts &mc, OutT *C, int64_t ldc,
+                                   const Layout &L, hipStream_t s, Ev ev) {
+    const int tiles_m = (int)((m + kFTile - 1) / kFTile), tiles_n = (int)((n + kFTile - 1) / kFTile);
+    auto kern = k_gemm_crt<OutT>;
+    OZ2_LAUNCH(ev, kern, dim3((unsigned)tiles_m * (unsigned)tiles_n), dim3(256), 0, s, RA, RB, L.m_pad * L.k_pad,
+               L.n_pad * L.k_pad, (int)(L.kb / 2), tiles_m, e, f, cc, mc, C, m, n, ldc);
+    return hipGetLastError();
+}
+
+bool gemm_crt_applies(const Layout &L, int64_t m, int64_t n) {
+    // the int32 sums of one modulus stay within smod's range for at most
+    // kReduceStages stages, and the grid is one block per 64 x 64 tile
+    return L.kb / 2 <= kReduceStages && ((m + kFTile - 1) / kFTile) * ((n + kFTile - 1) / kFTile) < (1ll << 31);
+}
+
+hipError_t launch_gemm_crt(Elem el, const int8_t *RA, const int8_t *RB, int64_t m, int64_t n, const int32_t *e,
+                           const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
+                           const Layout &L, hipStream_t s, Ev ev) {
+    if (el == Elem::f32) return launch_gemm_crt_t(RA, RB, m, n, e, f, cc, mc, (float *)C, ldc, L, s, ev);
+    return launch_gemm_crt_t(RA, RB, m, n, e, f, cc, mc, (double *)C, ldc, L, s, ev);
 }
 
 hipError_t launch_crt(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e, const int32_t *f,

@@ -77,6 +77,8 @@ CONFIGS = {
     "spread1.0_4096_n16": dict(m=4096, n=4096, k=4096, num_moduli=16, kind="spread", phi=1.0, seed=0),
     # 512^3, phi=1.0, N=14: a small product (the GEMM's 128 x 128 block shape).
     "spread1.0_512_n14": dict(m=512, n=512, k=512, num_moduli=14, kind="spread", phi=1.0, seed=0),
+    # 256^3, phi=1.0, N=14: a launch-bound product (one- vs two-launch steps 3-5).
+    "spread1.0_256_n14": dict(m=256, n=256, k=256, num_moduli=14, kind="spread", phi=1.0, seed=0),
     # 2048^3 scale sweep, N=14.
     "scale_sweep_2048_n14": dict(m=2048, n=2048, k=2048, num_moduli=14, kind="sweep", seed=0),
     # 16384^3, phi=1.0, N=18 (2 GiB per operand).
