@@ -42,10 +42,11 @@
  * two compute units a 256 x 256 block); OZ2_FUSED=1 runs steps 3-5 of real
  * products as one launch (every modulus of a 64 x 64 tile of C in one block,
  * reconstructed in registers; [Q] section 誤差のないINT8行列積(手順3): the
- * per-modulus products are independent), OZ2_FUSED=0 as two (the default
- * form, a 256 x 256 GEMM writing residue planes and a reconstruction reading
- * them); the debug entry points always use two. Results do not depend on
- * either setting.
+ * per-modulus products are independent), OZ2_FUSED=0 as two (a 256 x 256
+ * GEMM writing residue planes and a reconstruction reading them); by default
+ * one launch only for tiny products (N times the stages of 64 of k at most
+ * 16, at most 64 tiles of 64 x 64), two otherwise; the debug entry points
+ * always use two. Results do not depend on either setting.
  *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by
@@ -226,6 +227,49 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k,
 int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
                      const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * Test entry point: the CRT-range failure flag. An integer outside (-P/2, P/2]
+ * is silently reconstructed as another one ([Q] section
+ * 時計の針で見る定理の中身; [G] section Problemstellung: too large a scaling
+ * breaks the reconstruction). This runs ozaki2_dgemm_ws with num_moduli
+ * moduli and, beside them, the residue product for one redundant check
+ * modulus, the next one of the table (so num_moduli <= 19): the integer X the
+ * reconstruction returns for each entry must agree with that product modulo
+ * the check modulus, and cannot when X was wrapped by j*P, 0 < |j| < p_check.
+ * C is written exactly as ozaki2_dgemm_ws writes it.
+ *   flags_out DEVICE uint8 [n][m], entry (i, j) at flags_out[j*m + i]:
+ *             0 consistent, 1 the CRT range was exceeded (C is wrong there),
+ *             2 undecided (|X| within 2^-30 P of P/2, where the check's own
+ *             quotient may round either way; the fast and accurate scalings
+ *             keep |X| below (P-1)/2 * (1 - 2^-22), far from it).
+ *   workspace DEVICE, 256-byte aligned, ozaki2_check_workspace_size(...) bytes.
+ * Returns as ozaki2_dgemm_ws; -10 also for num_moduli = 20; -14 flags_out NULL
+ * while needed.
+ */
+int ozaki2_dgemm_check(int64_t m, int64_t n, int64_t k,
+                       const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode,
+                       void *workspace, size_t workspace_bytes, uint8_t *flags_out, void *stream);
+/* Bytes of workspace ozaki2_dgemm_check needs (0 for invalid arguments,
+ * num_moduli = 20 or empty products). Host-only. */
+size_t ozaki2_check_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
+
+/*
+ * Test entry point for the range check alone, on caller residues: as
+ * ozaki2_crt_debug with num_moduli + 1 residue planes, the last one for the
+ * check modulus (the (num_moduli+1)-th of the table), residues[(l*n + j)*m + i]
+ * in [0, p_l). C is reconstructed from the first num_moduli planes; flags_out
+ * as for ozaki2_dgemm_check.
+ * Returns 0; -1 m < 0, -2 n < 0, -3 num_moduli outside [2, 19], -4 residues,
+ * -5 e, -6 f, -7 C or -9 flags_out NULL while needed, -8 ldc < max(1, m),
+ * -10 workspace NULL or not 256-byte aligned; OZAKI2_ERR_WORKSPACE if
+ * workspace_bytes < ozaki2_check_workspace_size(m, n, 1, num_moduli,
+ * OZAKI2_FAST); OZAKI2_ERR_UNSUPPORTED; OZAKI2_ERR_HIP.
+ */
+int ozaki2_crt_check_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                           const int32_t *f, double *C, int64_t ldc, uint8_t *flags_out, void *workspace,
+                           size_t workspace_bytes, void *stream);
 
 /*
  * Single precision: C := A * B for binary32 A, B, C, emulated by the same

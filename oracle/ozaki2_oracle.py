@@ -461,6 +461,25 @@ def garner(c: np.ndarray, moduli) -> np.ndarray:
     return np.where(2 * X > P, X - P, X)
 
 
+def check_modulus(num_moduli: int) -> int:
+    """The redundant modulus of the range check: the next one of the table."""
+    return choose_moduli(num_moduli + 1)[num_moduli]
+
+
+def crt_range_flags(c: np.ndarray, c_check: np.ndarray, moduli, p_check: int) -> np.ndarray:
+    """CRT-range failure flags: 0 where the reconstruction agrees with one more clock, 1 where not.
+
+    [Q] section 時計の針で見る定理の中身: an integer Y outside (-P/2, P/2] is read
+    back as X = Y - j P, another number. With the residue c_check of the same
+    integer modulo a further modulus p_check (coprime to every p_l), X and Y
+    differ modulo p_check whenever 0 < |j| < p_check, so the flag is exactly
+    "X != Y" for such j. c holds the residues in [0, p_l) ([N][...]), c_check
+    the check residues in [0, p_check).
+    """
+    X = crt(c, crt_tables(moduli))
+    return np.where((X - np.asarray(c_check).astype(object)) % p_check == 0, 0, 1).astype(np.uint8)
+
+
 # --------------------------------------------------------------------------
 # Step 5 and the whole pipeline
 # --------------------------------------------------------------------------

@@ -33,7 +33,8 @@ EXPORTS = (
     "ozaki2_timing_read_calls",
     "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
     "ozaki2_zgemm", "ozaki2_zgemm_ws", "ozaki2_zgemm_debug", "ozaki2_cgemm", "ozaki2_cgemm_ws", "ozaki2_cgemm_debug",
-    "ozaki2_zgemm_workspace_size", "ozaki2_dgemm_noalloc",
+    "ozaki2_zgemm_workspace_size", "ozaki2_dgemm_noalloc", "ozaki2_dgemm_check", "ozaki2_check_workspace_size",
+    "ozaki2_crt_check_debug",
 )
 
 _lib = None
@@ -75,6 +76,12 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_zgemm_workspace_size.restype = sz
     L.ozaki2_crt_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, sz, p]
     L.ozaki2_crt_debug.restype = i32
+    L.ozaki2_dgemm_check.argtypes = prod + [p, sz, p, p]
+    L.ozaki2_dgemm_check.restype = i32
+    L.ozaki2_check_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+    L.ozaki2_check_workspace_size.restype = sz
+    L.ozaki2_crt_check_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, p, sz, p]
+    L.ozaki2_crt_check_debug.restype = i32
     L.ozaki2_max_moduli.argtypes = []
     L.ozaki2_max_moduli.restype = i32
     L.ozaki2_moduli.argtypes = [i32, p]
@@ -104,6 +111,22 @@ def ozaki2_dgemm(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) ->
 
 def ozaki2_dgemm_noalloc(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream=0) -> int:
     return lib().ozaki2_dgemm_noalloc(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, stream)
+
+
+def ozaki2_dgemm_check(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes, flags,
+                       stream=0) -> int:
+    return lib().ozaki2_dgemm_check(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                                    flags, stream)
+
+
+def ozaki2_check_workspace_size(m, n, k, num_moduli, mode) -> int:
+    return lib().ozaki2_check_workspace_size(m, n, k, num_moduli, mode)
+
+
+def ozaki2_crt_check_debug(m, n, num_moduli, residues, e, f, C, ldc, flags, workspace, workspace_bytes,
+                           stream=0) -> int:
+    return lib().ozaki2_crt_check_debug(m, n, num_moduli, residues, e, f, C, ldc, flags, workspace, workspace_bytes,
+                                        stream)
 
 
 def ozaki2_workspace_size(m, n, k, num_moduli, mode) -> int:

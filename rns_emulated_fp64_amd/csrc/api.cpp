@@ -155,15 +155,17 @@ Cache g_cache;
 
 // Steps 3-5 as one launch (k_gemm_crt: all moduli of a 64 x 64 tile per
 // block, reconstructed in registers) instead of the 256 x 256 GEMM writing
-// residue planes and a reconstruction launch reading them. OZ2_FUSED=1 or 0
-// in the environment forces either form; by default the two launches are
-// used, which measured faster at every size tried on MI355X.
-bool use_fused(const Layout &L, int64_t m, int64_t n) {
-    (void)L;
-    (void)m;
-    (void)n;
+// residue planes and a reconstruction launch reading them. A fused block runs
+// its N moduli one after another, so it wins only where the whole product is
+// a few stages long and the saved launch dominates: on MI355X 29 against
+// 34 us per product at 64^3 with 8 moduli (16 stages of 64 per block), but
+// 47 against 28 us at 256^3 and 14 moduli, and slower at every larger size
+// measured. Default: fused for N * (k stages) <= 16 and at most 64 tiles.
+// OZ2_FUSED=1 or 0 in the environment forces either form.
+bool use_fused(const Layout &L, int64_t m, int64_t n, int nmod) {
     if (const char *force = getenv("OZ2_FUSED")) return strcmp(force, "1") == 0;
-    return false;
+    const int64_t tiles = ((m + 63) / 64) * ((n + 63) / 64);
+    return (int64_t)nmod * (L.kb / 2) <= 16 && tiles <= 64;
 }
 
 struct DebugOut {
@@ -171,11 +173,17 @@ struct DebugOut {
     int8_t *ra, *rb;
     int32_t *prod;
     uint8_t *red;
+    uint8_t *check;  // CRT-range flags against one redundant modulus (ozaki2_dgemm_check)
 };
 
 int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int64_t lda, const void *B, int64_t ldb,
         void *C, int64_t ldc, int nmod, int mode, char *ws, const Layout &L, const DebugOut *dbg, hipStream_t s) {
     const Tables *T = get_tables(nmod);
+    // with the range check, the residues, products and reduced planes carry one
+    // more modulus (the next of the table) than the reconstruction uses
+    const bool check = dbg != nullptr && dbg->check != nullptr;
+    const Tables *TS = check ? get_tables(nmod + 1) : T;
+    const int nsplit = check ? nmod + 1 : nmod;
     // Timing events (start/stop per phase) ride on the first and the last
     // kernel launch of a phase; unless all phases were asked for, only the
     // GEMM phase is timed.
@@ -218,11 +226,11 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
 
     // Steps 1 + 2: integerize and split both operands into residues, one
     // launch (in fast mode it also finishes the row exponents of A).
-    HIP_TRY(launch_split(el, cplx, original, A, m, lda, B, n, ldb, k, !accurate, T->Pp, T->split, L, ws, s,
+    HIP_TRY(launch_split(el, cplx, original, A, m, lda, B, n, ldb, k, !accurate, T->Pp, TS->split, L, ws, s,
                          ev_of(kPhaseSplit, true, true)));
     const int32_t *e = (const int32_t *)(ws + L.e), *f = (const int32_t *)(ws + L.f);
 
-    if (!cplx && dbg == nullptr && use_fused(L, m, n) && gemm_crt_applies(L, m, n)) {
+    if (!cplx && dbg == nullptr && use_fused(L, m, n, nmod) && gemm_crt_applies(L, m, n)) {
         // Steps 3-5 in one launch: every modulus of a tile, reconstructed in registers.
         HIP_TRY(launch_gemm_crt(el, (const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), m, n, e, f, T->crt,
                                 T->mod, C, ldc, L, s, ev_of(kPhaseGemm, true, true)));
@@ -230,7 +238,7 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
     }
 
     // Step 3: one exact INT8 product per modulus, reduced mod p_l.
-    HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nmod, group, T->mod,
+    HIP_TRY(launch_gemm_mod((const int8_t *)(ws + L.ra), (const int8_t *)(ws + L.rb), nsplit, group, TS->mod,
                             (int8_t *)(ws + L.planes), L, s, ev_of(kPhaseGemm, true, true)));
 
     // Steps 4 + 5: reconstruction and unscaling.
@@ -240,6 +248,8 @@ int run(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, int6
     else
         HIP_TRY(launch_crt(el, (const int8_t *)(ws + L.planes), m, n, e, f, T->crt, C, ldc, L, s,
                            ev_of(kPhaseCrt, true, true)));
+
+    if (check) HIP_TRY(launch_crt_check((const int8_t *)(ws + L.planes), m, n, T->check, L, dbg->check, s));
 
     if (dbg) {
         if (dbg->e) HIP_TRY(hipMemcpyAsync(dbg->e, e, 4 * (size_t)m, hipMemcpyDeviceToDevice, s));
@@ -276,7 +286,8 @@ int front(Elem el, bool cplx, int64_t m, int64_t n, int64_t k, const void *A, in
         HIP_TRY(launch_zero_fill(el, C, cplx ? 2 * m : m, n, cplx ? 2 * ldc : ldc, s));
         return OZAKI2_SUCCESS;
     }
-    const Layout L = make_layout(m, n, k, nmod, mode, dbg != nullptr, cplx ? 3 : 1);
+    const bool check = dbg != nullptr && dbg->check != nullptr;
+    const Layout L = make_layout(m, n, k, check ? nmod + 1 : nmod, mode, dbg != nullptr && !check, cplx ? 3 : 1);
     if (!use_cache) {
         if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0) return -12;
         if (wbytes < L.total) return OZAKI2_ERR_WORKSPACE;
@@ -359,7 +370,7 @@ int ozaki2_dgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t
                        double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
-    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out, nullptr};
     return front(Elem::f64, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
                  false, &d, stream);
 }
@@ -381,7 +392,7 @@ int ozaki2_sgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t 
                        float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
-    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out, nullptr};
     return front(Elem::f32, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
                  false, &d, stream);
 }
@@ -411,6 +422,61 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
     return OZAKI2_SUCCESS;
 }
 
+size_t ozaki2_check_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode) {
+    if (num_moduli >= kMaxModuli) return 0;
+    if (validate(m, n, k, (const double *)1, m > 1 ? m : 1, (const double *)1, k > 1 ? k : 1, (const double *)1,
+                 m > 1 ? m : 1, num_moduli, mode))
+        return 0;
+    if (!layout_fits(m, n, k, mode) || m == 0 || n == 0 || k == 0) return 0;
+    return make_layout(m, n, k, num_moduli + 1, mode, false).total;
+}
+
+int ozaki2_dgemm_check(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
+                       double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
+                       uint8_t *flags_out, void *stream) {
+    int st = validate(m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode);
+    if (st) return st;
+    if (num_moduli >= kMaxModuli) return -10;  // the check modulus is the next one of the table
+    if (flags_out == nullptr && m > 0 && n > 0) return -14;
+    if (k == 0 && m > 0 && n > 0) {
+        // C = 0 exactly: nothing to reconstruct, every entry consistent
+        HIP_TRY(launch_zero_fill(Elem::f64, C, m, n, ldc, (hipStream_t)stream));
+        HIP_TRY(hipMemsetAsync(flags_out, 0, (size_t)m * (size_t)n, (hipStream_t)stream));
+        return OZAKI2_SUCCESS;
+    }
+    DebugOut d{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, flags_out};
+    return front(Elem::f64, false, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
+                 false, &d, stream);
+}
+
+int ozaki2_crt_check_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                           const int32_t *f, double *C, int64_t ldc, uint8_t *flags_out, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    if (m < 0) return -1;
+    if (n < 0) return -2;
+    if (num_moduli < 2 || num_moduli >= kMaxModuli) return -3;
+    const bool any = m > 0 && n > 0;
+    if (residues == nullptr && any) return -4;
+    if (e == nullptr && any) return -5;
+    if (f == nullptr && any) return -6;
+    if (C == nullptr && any) return -7;
+    if (ldc < (m > 1 ? m : 1)) return -8;
+    if (flags_out == nullptr && any) return -9;
+    if (!any) return OZAKI2_SUCCESS;
+    if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0) return -10;
+    if (!layout_fits(m, n, 1, OZAKI2_FAST)) return OZAKI2_ERR_UNSUPPORTED;
+    const Layout L = make_layout(m, n, 1, num_moduli + 1, OZAKI2_FAST, false);
+    if (workspace_bytes < L.total) return OZAKI2_ERR_WORKSPACE;
+    const Tables *T = get_tables(num_moduli);
+    const Tables *TS = get_tables(num_moduli + 1);
+    hipStream_t s = (hipStream_t)stream;
+    int8_t *planes = (int8_t *)((char *)workspace + L.planes);
+    HIP_TRY(launch_pack_planes(residues, num_moduli + 1, TS->mod, m, n, L, planes, s));
+    HIP_TRY(launch_crt(Elem::f64, planes, m, n, e, f, T->crt, C, ldc, L, s));
+    HIP_TRY(launch_crt_check(planes, m, n, T->check, L, flags_out, s));
+    return OZAKI2_SUCCESS;
+}
+
 int ozaki2_zgemm(int64_t m, int64_t n, int64_t k, const double *A, int64_t lda, const double *B, int64_t ldb,
                  double *C, int64_t ldc, int num_moduli, int mode, void *stream) {
     return front(Elem::f64, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, nullptr, 0, true, nullptr,
@@ -428,7 +494,7 @@ int ozaki2_zgemm_debug(int64_t m, int64_t n, int64_t k, const double *A, int64_t
                        double *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
-    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out, nullptr};
     return front(Elem::f64, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
                  false, &d, stream);
 }
@@ -450,7 +516,7 @@ int ozaki2_cgemm_debug(int64_t m, int64_t n, int64_t k, const float *A, int64_t 
                        float *C, int64_t ldc, int num_moduli, int mode, void *workspace, size_t workspace_bytes,
                        int32_t *e_out, int32_t *f_out, int8_t *resA_out, int8_t *resB_out, int32_t *prod_out,
                        uint8_t *red_out, void *stream) {
-    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out};
+    DebugOut d{e_out, f_out, resA_out, resB_out, prod_out, red_out, nullptr};
     return front(Elem::f32, true, m, n, k, A, lda, B, ldb, C, ldc, num_moduli, mode, workspace, workspace_bytes,
                  false, &d, stream);
 }

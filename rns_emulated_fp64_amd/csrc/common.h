@@ -54,6 +54,17 @@ struct CrtConsts {
     int8_t digit[kMaxDigits][32];   // digit[v][l] = v-th digit of W_l, |digit| <= 128; 0 for l >= n
 };
 
+// Constants of the CRT-range check against one redundant modulus pc (the
+// (n+1)-th of the table): X = S - q P with S / P = sum_l c_l K_l / p_l, so
+// X mod pc = sum_l c_l (W_l mod pc) - q (P mod pc) (mod pc).
+struct CheckConsts {
+    int n;                   // moduli of the reconstruction
+    int pc;                  // check modulus
+    double kp[kMaxModuli];   // RN(K_l / p_l), K_l = (P / p_l)^-1 mod p_l
+    int wm[kMaxModuli];      // W_l mod pc
+    int pm;                  // P mod pc
+};
+
 // Constants for the GEMM epilogue (reduction mod p_l).
 struct ModConsts {
     double p[kMaxModuli];
@@ -125,6 +136,11 @@ hipError_t launch_gemm_crt(Elem el, const int8_t *RA, const int8_t *RB, int64_t 
 hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t n, const int32_t *e,
                               const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
                               const Layout &L, hipStream_t s, Ev ev = {});
+// flags[j*m + i]: 0 the reconstruction of entry (i, j) from the first ck.n
+// planes agrees with plane ck.n (the check modulus), 1 it does not (the
+// integer left (-P/2, P/2]), 2 undecided (|X| at P/2 within 2^-30 P).
+hipError_t launch_crt_check(const int8_t *planes, int64_t m, int64_t n, const CheckConsts &ck, const Layout &L,
+                            uint8_t *flags, hipStream_t s);
 hipError_t launch_zero_fill(Elem el, void *C, int64_t m, int64_t n, int64_t ldc, hipStream_t s);
 hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, int64_t k,
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);

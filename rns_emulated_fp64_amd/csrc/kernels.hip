@@ -1361,6 +1361,39 @@ __global__ __launch_bounds__(256) void k_crt_c(const int8_t *__restrict__ planes
     }
 }
 
+// CRT-range check against one redundant modulus (debug entry points): the
+// integer X the reconstruction returns from the first ck.n residues must agree
+// with the residue product of the check modulus pc ([Q] section
+// 時計の針で見る定理の中身: outside (-P/2, P/2] the clocks show another number;
+// [G] Problemstellung: too large a scaling breaks the reconstruction). X =
+// S - q P with q = round(S / P) and S / P = sum_l c_l K_l / p_l, whose FP64 sum
+// is good to ~2^-44, so q is the reconstruction's own quotient unless |X| lies
+// within 2^-30 P of P / 2 (flag 2). X mod pc follows exactly in int32 from
+// W_l mod pc and P mod pc. A wrapped X = Y - j P (0 < |j| < pc) always
+// disagrees, since pc does not divide j P.
+__global__ __launch_bounds__(256) void k_crt_check(const int8_t *__restrict__ planes, int64_t plane_elems,
+                                                   int64_t m_pad, int64_t m, int64_t n, CheckConsts ck,
+                                                   uint8_t *__restrict__ flags) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= m) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i;
+        double sp = 0.0;
+        int xm = 0;
+        for (int l = 0; l < ck.n; ++l) {
+            const int c = src[(int64_t)l * plane_elems];
+            sp = fma((double)c, ck.kp[l], sp);
+            xm += c * ck.wm[l];
+        }
+        const double q = rint(sp);
+        const int cc = src[(int64_t)ck.n * plane_elems];
+        int r = (xm - (int)q * ck.pm - cc) % ck.pc;
+        uint8_t flag = r == 0 ? 0 : 1;
+        if (fabs(sp - q) > 0.5 - 0x1p-30) flag = 2;
+        flags[j * m + i] = flag;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Steps 3 + 4 + 5 fused: all moduli of one output tile in one block
 // ---------------------------------------------------------------------------
@@ -1829,6 +1862,13 @@ hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts
                               const Layout &L, int8_t *planes, hipStream_t s) {
     dim3 grid(nblk(L.m_pad, 256), ydim(n), (unsigned)nmod);
     hipLaunchKernelGGL(k_pack_planes, grid, dim3(256), 0, s, residues, m, n, L.m_pad, L.m_pad * L.n_pad, mc, planes);
+    return hipGetLastError();
+}
+
+hipError_t launch_crt_check(const int8_t *planes, int64_t m, int64_t n, const CheckConsts &ck, const Layout &L,
+                            uint8_t *flags, hipStream_t s) {
+    hipLaunchKernelGGL(k_crt_check, dim3(nblk(m, 256), ydim(n)), dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad,
+                       m, n, ck, flags);
     return hipGetLastError();
 }
 

@@ -206,6 +206,27 @@ void build(Tables &t, int n) {
         t.crt.P32[c] = (double)P.d[c];
         t.crt.H32[c] = (double)H.d[c];
     }
+
+    // check against the next modulus of the table ([Q] section
+    // 時計の針で見る定理の中身: an integer outside (-P/2, P/2] comes back as
+    // another one; one more clock tells the two apart)
+    if (n < kMaxModuli) {
+        int32_t next[kMaxModuli];
+        greedy_moduli(n + 1, next);
+        const int pc = next[n];
+        t.check.n = n;
+        t.check.pc = pc;
+        t.check.pm = (int)P.mod_small((uint32_t)pc);
+        for (int l = 0; l < n; ++l) {
+            U256 W;
+            std::memcpy(W.d, t.weight[l], sizeof(W.d));
+            t.check.wm[l] = (int)W.mod_small((uint32_t)pc);
+            uint32_t r;
+            const U256 M = P.div_small((uint32_t)t.moduli[l], &r);
+            const int64_t K = inverse_mod(M.mod_small((uint32_t)t.moduli[l]), t.moduli[l]);
+            t.check.kp[l] = (double)K / (double)t.moduli[l];
+        }
+    }
 }
 
 std::mutex g_mu;

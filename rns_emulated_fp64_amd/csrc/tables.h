@@ -18,6 +18,7 @@ struct Tables {
     SplitConsts split{};
     CrtConsts crt{};
     ModConsts mod{};
+    CheckConsts check{};  // against modulus n + 1 (n < kMaxModuli only)
 };
 
 // Fills out[0..n) with the n largest pairwise-coprime integers <= 256 taken

@@ -44,6 +44,20 @@ def test_no_library_symbol_left_undefined():
     assert "oz2" not in out, [l for l in out.splitlines() if "oz2" in l][:4]
 
 
+def test_check_entry_host_checks():
+    assert oz.ozaki2_check_workspace_size(64, 64, 64, 20, 0) == 0  # no 21st modulus
+    assert oz.ozaki2_check_workspace_size(64, 64, 64, 16, 0) > oz.ozaki2_workspace_size(64, 64, 64, 16, 0)
+    need = oz.ozaki2_check_workspace_size(64, 64, 64, 16, 0)
+    assert oz.ozaki2_dgemm_check(64, 64, 64, P, 64, P, 64, P, 64, 20, 0, P, need, P, 0) == -10
+    assert oz.ozaki2_dgemm_check(64, 64, 64, P, 64, P, 64, P, 64, 16, 0, P, need, 0, 0) == -14
+    assert oz.ozaki2_dgemm_check(64, 64, 64, P, 64, P, 64, P, 64, 16, 0, P + 64, need, P, 0) == -12
+    assert oz.ozaki2_dgemm_check(64, 64, 64, P, 64, P, 64, P, 64, 16, 0, P, need - 1, P, 0) == 2
+    assert oz.ozaki2_crt_check_debug(4, 4, 20, P, P, P, P, 4, P, P, 1 << 40, 0) == -3
+    assert oz.ozaki2_crt_check_debug(4, 4, 8, P, P, P, P, 4, 0, P, 1 << 40, 0) == -9
+    assert oz.ozaki2_crt_check_debug(4, 4, 8, P, P, P, P, 4, P, P + 8, 1 << 40, 0) == -10
+    assert oz.ozaki2_crt_check_debug(4, 4, 8, P, P, P, P, 4, P, P, 16, 0) == 2
+
+
 def test_noalloc_host_checks():
     # argument errors and the array limit come back before any HIP call
     assert oz.ozaki2_dgemm_noalloc(-1, 4, 4, P, 4, P, 4, P, 4, 8, 0, 0) == -1

@@ -187,3 +187,51 @@ def test_error_metrics_hand_worked_2x2():
     C2 = C.copy()
     C2[1, 1] = 2.0 ** -1000
     assert O.error_metrics(C2, hi, lo, A, B)["E_cw"] == math.inf
+
+
+# ---------------------------------------------------------------- CRT range check
+@pytest.mark.parametrize("moduli,p_check", [([3, 5, 7], 11), ([256, 255], 253), ([4, 3, 5, 7], 11)])
+def test_range_flags_brute_force(moduli, p_check):
+    """Every integer Y in [-2P, 2P]: the flag is set exactly when Y lies outside
+    (-P/2, P/2] ([Q] section 時計の針で見る定理の中身: such Y is read back as
+    another number). Planted: a lift to [0, P) instead of (-P/2, P/2] flags
+    the negative half and fails here (and in the table-edge test below)."""
+    P = math.prod(moduli)
+    Y = np.arange(-2 * P, 2 * P + 1, dtype=np.int64)
+    c = np.stack([np.mod(Y, p) for p in moduli]).astype(np.int64)
+    flags = O.crt_range_flags(c, np.mod(Y, p_check), moduli, p_check)
+    outside = ~((2 * Y > -P) & (2 * Y <= P))
+    assert np.array_equal(flags.astype(bool), outside)
+
+
+def test_range_flags_with_the_table_edges():
+    # N = 16 and its check modulus, the 17th of the table (191 in the footnote's order)
+    N = 16
+    moduli = O.choose_moduli(N)
+    pc = O.check_modulus(N)
+    assert pc == 191
+    P = math.prod(moduli)
+    H = P // 2
+    Y = [0, 1, -1, H, -H + 1, H - 1, H + 1, -H, P, -P, 3 * H, 190 * P + 5]
+    want = [0, 0, 0, 0, 0, 0, 1, 1, 1, 1, 1, 1]
+    c = np.array([[y % p for y in Y] for p in moduli], dtype=object)
+    flags = O.crt_range_flags(c, np.array([y % pc for y in Y], dtype=object), moduli, pc)
+    assert flags.tolist() == want
+
+
+def test_range_flags_catch_a_planted_exponent_error():
+    # one bit too many on every row of a ones product: the reconstruction wraps
+    # (X != Y everywhere) and the flags say so; with the right exponents none is set
+    k, N = 2048, 14
+    A = np.ones((4, k))
+    B = np.ones((k, 4))
+    moduli = O.choose_moduli(N)
+    pc = O.check_modulus(N)
+    e, f = O.exponents(A, B, N, "fast")
+    for shift, want in ((0, 0), (1, 1)):
+        ee = [v + shift for v in e]
+        r = O.os2_dgemm(A, B, N, e=ee, f=f)
+        Y = O.exact_scaled_product(A, B, r["e"], r["f"])
+        flags = O.crt_range_flags(r["c"], np.mod(Y, pc), moduli, pc)
+        assert np.all(flags == want)
+        assert np.array_equal(flags.astype(bool), r["X"] != Y)
