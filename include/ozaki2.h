@@ -46,7 +46,10 @@
  * GEMM writing residue planes and a reconstruction reading them); by default
  * one launch only for tiny products (N times the stages of 64 of k at most
  * 16, at most 64 tiles of 64 x 64), two otherwise; the debug entry points
- * always use two. Results do not depend on either setting.
+ * always use two. OZ2_GEMM_KERNEL=blocks runs the 256 x 256 tile one tile per
+ * block (eight wavefronts) instead of on the default persistent kernel (one
+ * block of four wavefronts per compute unit walking its tiles). Results do not
+ * depend on any of these settings.
  *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by

@@ -730,11 +730,12 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // block barrier at the end of the stage leaves two stages in flight. The
 // 16 x 16 x 64 form is used rather than 32 x 32 x 32 because on random
 // residues MI355X sustains more INT8 throughput with it under its power
-// limit (it moves less accumulator data per operation), and two waves per
-// SIMD because a wave's LDS reads hardly overlap its own MFMAs while another
-// wave's MFMAs cover them. The grid runs over (modulus, tile row, tile
-// column); block ids are remapped so each XCD works through a compact group
-// of tiles of one modulus and its L2 serves the shared A and B panels.
+// limit (it moves less accumulator data per operation). The grid runs over
+// (modulus, tile row, tile column); block ids are remapped so each XCD works
+// through a compact group of tiles of one modulus and its L2 serves the shared
+// A and B panels. Launches of four or more stages run the 256 x 256 tile on the
+// persistent one-wave-per-SIMD kernel further below (k_gemm_persistent), which
+// keeps this kernel's ring, tile order and epilogue.
 constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
 constexpr int kNST = 5;                    // LDS stages in the ring
 constexpr int kLoadsPerWave = 4;           // 1 KiB copies per wave per stage (both tile shapes)
@@ -745,23 +746,26 @@ constexpr int kReduceStages = 1024;        // stages per launch: 1024 * 64 * 2^1
 #define OZ2_GEMM_VMCNT "8"
 static_assert((kNST - 3) * kLoadsPerWave == 8, "OZ2_GEMM_VMCNT must equal (kNST - 3) * kLoadsPerWave");
 
-// A block shape: WM x WN wavefronts, each owning RT x CT MFMA tiles of 16 x 16.
-template <int WM_, int WN_, int RT_, int CT_>
+// A block shape: WM x WN wavefronts, each owning RT x CT MFMA tiles of 16 x 16
+// and issuing LPW 1 KiB copies per stage.
+template <int WM_, int WN_, int RT_, int CT_, int LPW_ = kLoadsPerWave>
 struct GemmShape {
-    static constexpr int WM = WM_, WN = WN_, RT = RT_, CT = CT_;
+    static constexpr int WM = WM_, WN = WN_, RT = RT_, CT = CT_, LPW = LPW_;
     static constexpr int W = WM * WN;                        // wavefronts per block
     static constexpr int TM = WM * RT * 16, TN = WN * CT * 16;  // block tile
     static constexpr int FA = TM / 16, FB = TN / 16;         // fragment blocks per stage
     static constexpr int STAGE = (FA + FB) * 1024;           // bytes per LDS stage
     static constexpr int NF = RT + CT;                       // fragments a wave reads per stage
     static constexpr int NQ = RT * CT;                       // MFMAs per wave per stage
-    static_assert(FA == FB && FA == (W / 2) * kLoadsPerWave, "half the waves copy A, half B");
+    static_assert(FA == FB && FA == (W / 2) * LPW, "half the waves copy A, half B");
     static_assert(kNST * STAGE <= 160 * 1024, "the ring must fit in LDS");
-    static_assert(NQ % kLoadsPerWave == 0 && NF % kLoadsPerWave == 0, "copies and reads spread evenly");
+    static_assert(NQ % LPW == 0 && NF % LPW == 0, "copies and reads spread evenly");
     static_assert(RT % 4 == 0, "the epilogue transposes groups of four row tiles");
 };
-using ShapeL = GemmShape<2, 4, 8, 4>;  // 256 x 256, 8 waves of 128 x 64
-using ShapeS = GemmShape<2, 2, 4, 4>;  // 128 x 128, 4 waves of 64 x 64
+using ShapeL = GemmShape<2, 4, 8, 4>;     // 256 x 256, 8 waves of 128 x 64
+using ShapeS = GemmShape<2, 2, 4, 4>;     // 128 x 128, 4 waves of 64 x 64
+using ShapeP = GemmShape<2, 2, 8, 8, 8>;  // 256 x 256, 4 waves of 128 x 128 (persistent kernel)
+static_assert(ShapeP::TM == ShapeL::TM && ShapeP::TN == ShapeL::TN, "both large kernels cover one tile grid");
 
 enum { EPI_MOD = 0, EPI_RAW = 1, EPI_BOUND = 2 };
 
@@ -821,9 +825,19 @@ __device__ __forceinline__ int smod(int q, double pinv, int p) {
 // stacked in rows, the four lanes L % 16 + 16 q trade words in a 4 x 4
 // transpose (two exchange rounds, across lanes L ^ 32 and L ^ 16) so that
 // each ends with the 16 consecutive rows of one tile.
-template <int RT, int CT>
+// LANE32: the lane's part of the address, (L % 16) m_pad + 16 (L / 16), fits
+// 32 bits (m_pad < 2^27) and is added to a wave-uniform tile address, which
+// keeps the address arithmetic in scalar registers and one VGPR.
+template <int RT, int CT, bool LANE32 = false>
 __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[RT][CT], int p, double pinv, int8_t *plane,
                                                 int64_t m_pad, int row0, int col0, int lane, bool accumulate) {
+    // LANE32 re-derives the lane index here (v_mbcnt, opaque to the optimiser) so
+    // that neither it nor an address built from it stays live across a caller's
+    // loop, where every VGPR is taken
+    int ln = lane;
+    if constexpr (LANE32)
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const uint32_t lane_elem = (uint32_t)(ln & 15) * (uint32_t)m_pad + 16u * (uint32_t)(ln >> 4);
 #pragma unroll
     for (int j = 0; j < CT; ++j)
 #pragma unroll
@@ -847,8 +861,12 @@ __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[RT][CT], int p,
             w[2] = q1[0];
             w[3] = q1[1];
             // now w[c] = rows 4c .. 4c + 3 of tile 4g + L/16
-            uint4 *dst = (uint4 *)(plane + (int64_t)(col0 + 16 * j + (lane & 15)) * m_pad + row0 +
-                                   16 * (4 * g + (lane >> 4)));
+            uint4 *dst;
+            if constexpr (LANE32)
+                dst = (uint4 *)(plane + (int64_t)(col0 + 16 * j) * m_pad + (row0 + 64 * g) + lane_elem);
+            else
+                dst = (uint4 *)(plane + (int64_t)(col0 + 16 * j + (lane & 15)) * m_pad + row0 +
+                                16 * (4 * g + (lane >> 4)));
             if (accumulate) {
                 // a later block of the inner dimension: add the residues of the
                 // earlier blocks (|sum| <= 256) and reduce again
@@ -1000,6 +1018,174 @@ __global__ __launch_bounds__(64 * SH::W) __attribute__((amdgpu_waves_per_eu(2, 2
             if (lane < 16) atomicMax(&ga.colmax[col0 + 16 * j + lane], mx);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Step 3, persistent form of the 256 x 256 tile: one block per compute unit
+// walks the tiles bid = blockIdx.x + i * gridDim.x (the same XCD-aware order
+// as k_gemm's grid). Four wavefronts, one per SIMD, each own a 128 x 128
+// quarter (8 x 8 MFMA tiles, 256 accumulators per lane), so every fragment
+// read from LDS feeds eight MFMAs instead of six (a third fewer LDS bytes per
+// operation than k_gemm's 128 x 64). The five-slot copy ring runs on across
+// tile boundaries: the first four stages of the next tile are copied during the
+// last four stages of the current one and land while its epilogue runs.
+//
+// With one wavefront per SIMD nothing else issues while this one waits, so the
+// stage schedule spreads the work between MFMAs: the block barrier for the next
+// stage after the 4th MFMA, one fragment read every 3rd MFMA from the 5th, one
+// copy every 6th MFMA from the 6th. The copies take their source address from
+// scalar registers (the saddr form of global_load_lds_dwordx4, the lane offset in
+// one VGPR), which keeps vector address arithmetic and scalar/vector hazards out
+// of the MFMA stream.
+//
+// Counter waits: vector-memory operations of a wavefront complete in issue
+// order, so waiting for a stage's copies means allowing only the operations
+// issued after them: the copies of the two later stages (16), plus, in the
+// first three stages of a tile, the 16 stores of the previous tile's epilogue
+// that were issued between them. Requires nks >= kNST - 1 (and even), so the
+// copies never reach beyond the next tile.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+    static_assert(N == 16 || N == 32, "add the count");
+    if constexpr (N == 16)
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_persistent(
+        GemmArgs ga, ModConsts mc) {
+    constexpr int RT = ShapeP::RT, CT = ShapeP::CT, NF = ShapeP::NF, NQ = ShapeP::NQ, FA = ShapeP::FA;
+    constexpr int FB = ShapeP::FB, STAGE = ShapeP::STAGE, LPW = ShapeP::LPW, W = ShapeP::W, WN = ShapeP::WN;
+    constexpr int TM = ShapeP::TM, TN = ShapeP::TN;
+    constexpr int VMC = (kNST - 3) * LPW;  // copies of the two stages after the one read next
+    constexpr int NSTORE = RT * CT / 4;    // 16-byte stores of one epilogue
+    constexpr int PRE = 4, RSTEP = 3, CSTEP = 6;
+    static_assert(PRE + RSTEP * (NF - 1) < NQ && PRE + 1 + CSTEP * (LPW - 1) < NQ, "schedule fits a stage");
+    __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * STAGE];
+
+    const int total = ga.tiles_m * ga.tiles_n * ga.nmod;
+    const int G = gridDim.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const int nk = ga.nks;
+    const int64_t row_bytes = (ga.kb / 2) * 1024;  // one 16-row block over all of K
+    const bool copies_a = wave < W / 2;
+    const int wq = wave % (W / 2);
+    // wave-uniform source of this wave's copies for tile b at stage 0 of the launch
+    auto source = [&](int b, int &l, int &tm, int &tn) -> const int8_t * {
+        decode_block(b, total, ga.tiles_m, ga.tiles_n, l, tm, tn);
+        return (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * FA + wq * LPW) * row_bytes
+                         : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * FB + wq * LPW) * row_bytes) +
+               ga.ks0 * 1024;
+    };
+    __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
+    const uint32_t lane_off = (uint32_t)lane * 16u;
+    // copy q of a stage: 1 KiB from src + q * row_bytes + lane * 16 into ring slot `slot`
+    auto dma = [&](const int8_t *src, int slot, int q) {
+        const uint64_t a = (uint64_t)(uintptr_t)(src + q * row_bytes);
+        const uint32_t dst = (uint32_t)(uintptr_t)(lds3 + slot * STAGE + (wave * LPW + q) * 1024);
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :: "v"(lane_off), "s"(a), "s"(dst) : "memory", "m0");
+    };
+    auto frag = [&](const int8_t *st, int r) {
+        return *(const v4i *)(st + (r < RT ? wm * RT + r : FA + wn * CT + (r - RT)) * 1024 + lane * 16);
+    };
+
+    int bid = blockIdx.x;
+    int l, tm, tn, nl = 0, ntm = 0, ntn = 0;
+    const int8_t *cur = source(bid, l, tm, tn);
+    int nbid = bid + G;
+    const int8_t *nxt = nbid < total ? source(nbid, nl, ntm, ntn) : cur;
+    // source of the copies issued during stage ks: stage ks + kNST - 1 of this
+    // tile or of the next; past the last tile, a copy of this tile's last stage
+    // into a slot that is never read (keeps the counter waits constant)
+    auto copy_src = [&](int ks) -> const int8_t * {
+        const int t = ks + kNST - 1;
+        if (t < nk) return cur + t * 1024;
+        if (nbid < total) return nxt + (t - nk) * 1024;
+        return cur + (nk - 1) * 1024;
+    };
+
+    v4i acc[RT][CT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < CT; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int st = 0; st < kNST - 1; ++st)
+#pragma unroll
+        for (int q = 0; q < LPW; ++q) dma(cur + st * 1024, st, q);
+    vm_wait_barrier<VMC>();  // stages 0 and 1 landed
+    v4i f0[NF], f1[NF];      // fragments of the current / next stage: A tiles, then B tiles
+#pragma unroll
+    for (int r = 0; r < NF; ++r) f0[r] = frag(lds, r);
+
+    int slot = 0;  // ring slot of the current stage
+    // stage ks: MFMAs on fc; after the barrier, reads of the next stage into fn
+    // (B fragments first) and the copies for stage ks + kNST - 1 into the slot
+    // the previous stage used. after_epi: the previous epilogue's stores were
+    // issued after the copies this stage waits for.
+    auto stage = [&](int ks, v4i(&fc)[NF], v4i(&fn)[NF], bool after_epi) {
+        const int nslot = slot == kNST - 1 ? 0 : slot + 1;
+        const int cslot = slot == 0 ? kNST - 1 : slot - 1;
+        const int8_t *next = lds + nslot * STAGE;
+        const int8_t *src = copy_src(ks);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            acc[q / CT][q % CT] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q / CT], fc[RT + q % CT],
+                                                                       acc[q / CT][q % CT], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q == PRE - 1) {
+                if (after_epi)
+                    vm_wait_barrier<VMC + NSTORE>();
+                else
+                    vm_wait_barrier<VMC>();
+            }
+            if (q >= PRE && (q - PRE) % RSTEP == 0 && (q - PRE) / RSTEP < NF) {
+                const int i = (q - PRE) / RSTEP;
+                const int r = i < CT ? RT + i : i - CT;
+                fn[r] = frag(next, r);
+            }
+            if (q > PRE && (q - PRE - 1) % CSTEP == 0 && (q - PRE - 1) / CSTEP < LPW)
+                dma(src, cslot, (q - PRE - 1) / CSTEP);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        slot = nslot;
+    };
+
+    bool after_epi = false;
+    while (true) {
+        stage(0, f0, f1, after_epi);
+        stage(1, f1, f0, after_epi);
+        stage(2, f0, f1, after_epi);
+        stage(3, f1, f0, false);
+        for (int ks = 4; ks < nk; ks += 2) {
+            stage(ks, f0, f1, false);
+            stage(ks + 1, f1, f0, false);
+        }
+        const int row0 = tm * TM + wm * RT * 16, col0 = tn * TN + wn * CT * 16;
+        store_mod_tiles<RT, CT, true>(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group],
+                                      ga.planes + (int64_t)l * ga.plane_elems, ga.m_pad, row0, col0, lane,
+                                      ga.accumulate != 0);
+        after_epi = true;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int j = 0; j < CT; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
+        bid = nbid;
+        if (bid >= total) break;
+        cur = nxt;
+        l = nl;
+        tm = ntm;
+        tn = ntn;
+        nbid = bid + G;
+        if (nbid < total) nxt = source(nbid, nl, ntm, ntn);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
 }
 
 // ---------------------------------------------------------------------------
@@ -1695,11 +1881,8 @@ hipError_t launch_quantize(Elem el, const void *A, int64_t m, int64_t lda, const
 // traffic per MFMA costs more than the fuller chip gains). OZ2_GEMM_TILE=128
 // or 256 in the environment forces a shape; the results do not depend on it
 // (the tests run both shapes at every size).
-static bool use_small_tiles(const Layout &L, int planes) {
-    if (const char *force = getenv("OZ2_GEMM_TILE")) {
-        if (strcmp(force, "128") == 0) return true;
-        if (strcmp(force, "256") == 0) return false;
-    }
+// Compute units of the current device (cached per device).
+static int compute_units() {
     static std::atomic<int> cu_count[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1709,8 +1892,25 @@ static bool use_small_tiles(const Layout &L, int planes) {
             cus = 256;
         cu_count[dev].store(cus, std::memory_order_relaxed);
     }
+    return cus;
+}
+
+static bool use_small_tiles(const Layout &L, int planes) {
+    if (const char *force = getenv("OZ2_GEMM_TILE")) {
+        if (strcmp(force, "128") == 0) return true;
+        if (strcmp(force, "256") == 0) return false;
+    }
     const int64_t blocks = (L.m_pad / ShapeL::TM) * (L.n_pad / ShapeL::TN) * (int64_t)planes;
-    return 2 * blocks <= (int64_t)cus;
+    return 2 * blocks <= (int64_t)compute_units();
+}
+
+// The 256 x 256 tile runs on the persistent kernel when a launch has at least
+// kNST - 1 stages (and m_pad < 2^27, for its 32-bit lane offsets);
+// OZ2_GEMM_KERNEL=blocks forces the one-tile-per-block kernel.
+static bool use_persistent(int nks, int64_t m_pad) {
+    if (nks < kNST - 1 || m_pad >= ((int64_t)1 << 27)) return false;
+    const char *force = getenv("OZ2_GEMM_KERNEL");
+    return !(force && strcmp(force, "blocks") == 0);
 }
 
 static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L, bool small) {
@@ -1750,6 +1950,10 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
         if (small) {
             auto kern = k_gemm<EPI_MOD, ShapeS>;
             OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
+        } else if (use_persistent(g.nks, L.m_pad)) {
+            // one block per compute unit (the kernel's 160 KiB of LDS admits no second)
+            const int grid = blocks < compute_units() ? blocks : compute_units();
+            OZ2_LAUNCH(e, k_gemm_persistent, dim3(grid), dim3(64 * ShapeP::W), 0, s, g, mc);
         } else {
             auto kern = k_gemm<EPI_MOD, ShapeL>;
             OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeL::W), 0, s, g, mc);

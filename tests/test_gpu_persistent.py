@@ -1,0 +1,87 @@
+"""The persistent form of the 256 x 256 INT8 GEMM (one block per compute unit
+walking its tiles, the copy ring running across tile boundaries; the default
+for launches of at least four 64-deep stages) against the one-tile-per-block
+kernel (OZ2_GEMM_KERNEL=blocks) and against the oracle: the reduced residue
+planes and C bit-identical. Shapes cover one tile per block, a grid of more
+tiles than compute units (blocks walking two tiles, a ragged last round), the
+shortest inner dimension it takes (four stages), an inner dimension split into
+accumulating launches whose second one still has four or more stages, and
+complex products (three planes per modulus).
+
+Pages: [Q] step 3 (one exact INT8 product per modulus, reduced mod p)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_util import assert_bitwise_equal, full_parity, run_debug
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _both_kernels(monkeypatch, A, B, N, mode="fast"):
+    monkeypatch.setenv("OZ2_GEMM_TILE", "256")
+    monkeypatch.setenv("OZ2_GEMM_KERNEL", "blocks")
+    g0 = run_debug(A, B, N, mode, want_prod=False, want_res=False)
+    monkeypatch.delenv("OZ2_GEMM_KERNEL")
+    g1 = run_debug(A, B, N, mode, want_prod=False, want_res=False)
+    assert np.array_equal(g1["red"], g0["red"]), "reduced residue planes differ between the two kernels"
+    assert_bitwise_equal(g1["C"], g0["C"], "C (persistent vs blocks)")
+    return g1
+
+
+# (m, n, k, N): tiles = ceil(m/256) * ceil(n/256) * N
+SHAPES = [
+    (256, 256, 256, 2),      # one tile per block, exactly four stages
+    (300, 200, 200, 8),      # ragged edges, k padded to 256
+    (700, 530, 390, 20),     # 3 x 3 x 20 = 180 tiles
+    (1100, 1100, 300, 11),   # 5 x 5 x 11 = 275 tiles: 19 blocks walk a second tile
+    (1024, 1024, 1000, 20),  # 320 tiles, 16 stages
+]
+
+
+@pytest.mark.parametrize("m,n,k,N", SHAPES)
+def test_persistent_equals_blocks_kernel(monkeypatch, m, n, k, N):
+    A, B = W.spread_case(m, n, k, 1.0, seed=m + n + k + N)
+    _both_kernels(monkeypatch, A, B, N)
+
+
+def test_persistent_accurate_mode(monkeypatch):
+    A, B = W.spread_case(600, 900, 700, 2.0, seed=41)
+    _both_kernels(monkeypatch, A, B, 16, "accurate")
+
+
+def test_persistent_walking_tiles_against_oracle():
+    # 4 x 4 tiles x 17 moduli = 272 > 256 blocks, so some blocks take a second
+    # tile and its first stages are copied during the first tile's epilogue
+    A, B = W.spread_case(1024, 1024, 300, 1.0, seed=17)
+    full_parity(A, B, 17, want_prod=False)
+
+
+def test_persistent_split_inner_dimension(monkeypatch):
+    # k_pad = 65536 + 384: launches of 1024 and 6 stages; the second one adds
+    # to the residues of the first (the accumulating epilogue) and is still
+    # long enough for the persistent kernel
+    k = 65536 + 300
+    A, B = W.spread_case(260, 40, k, 0.5, seed=3)
+    g = _both_kernels(monkeypatch, A, B, 8)
+    assert_bitwise_equal(g["C"], O.os2_dgemm(A, B, 8)["C"], "C against the oracle")
+
+
+def test_persistent_complex(monkeypatch):
+    from test_gpu_zgemm import complex_case, run_complex
+    A, B = complex_case(530, 280, 400, 7)
+    monkeypatch.setenv("OZ2_GEMM_TILE", "256")
+    monkeypatch.setenv("OZ2_GEMM_KERNEL", "blocks")
+    g0 = run_complex(A, B, 14, want_prod=False)
+    monkeypatch.delenv("OZ2_GEMM_KERNEL")
+    g1 = run_complex(A, B, 14, want_prod=False)
+    assert np.array_equal(g1["red"], g0["red"]), "reduced planes differ"
+    assert_bitwise_equal(g1["C_re"], g0["C_re"], "Re C")
+    assert_bitwise_equal(g1["C_im"], g0["C_im"], "Im C")
