@@ -71,13 +71,20 @@ def gemm_source_hash():
     return hashlib.sha256((code(sec) + "\n" + code(common)).encode()).hexdigest()
 
 
+def gemm_kernel_name():
+    """The INT8 GEMM kernel the headline workload runs on (256 x 256 tiles, more
+    than four 64-deep stages): the persistent one unless OZ2_GEMM_KERNEL=blocks."""
+    return "k_gemm<EPI_MOD>" if os.environ.get("OZ2_GEMM_KERNEL") == "blocks" else "k_gemm_persistent"
+
+
 def gemm_traffic_bytes():
     """HBM bytes per GEMM launch from the committed counter runs, or None.
 
     The figure is used only while the GEMM's code still hashes to the one the
     counters were taken on.
     """
-    path = os.path.join(ROOT, "profiles", "k_gemm_spread1.0_4096_n16_traffic.txt")
+    stem = "k_gemm" if gemm_kernel_name() == "k_gemm<EPI_MOD>" else gemm_kernel_name()
+    path = os.path.join(ROOT, "profiles", f"{stem}_spread1.0_4096_n16_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -425,7 +432,7 @@ def main():
     traffic = gemm_traffic_bytes() if args.config == "spread1.0_4096_n16" and args.mode == "fast" else None
     roofline = dict(bound="mfma", achieved=round(gemm_tops, 2), peak=INT8_PEAK_TOPS, unit="TFLOP/s",
                     frac=round(gemm_tops / INT8_PEAK_TOPS, 4), traffic=traffic,
-                    kernel="k_gemm<EPI_MOD>", ops_per_launch=int8_ops, dtype="int8")
+                    kernel=gemm_kernel_name(), ops_per_launch=int8_ops, dtype="int8")
 
     C = dC.cpu().numpy().T  # C of the last step
     extras = {}

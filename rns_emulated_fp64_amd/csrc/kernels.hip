@@ -883,6 +883,9 @@ __device__ __forceinline__ void store_mod_tiles(const v4i (&acc)[RT][CT], int p,
                 }
             }
             *dst = make_uint4(w[0], w[1], w[2], w[3]);
+            // one group of four tiles at a time: keeps the accumulator reads
+            // from being hoisted into one register-hungry block
+            if constexpr (LANE32) __builtin_amdgcn_sched_barrier(0);
         }
 }
 
@@ -1030,28 +1033,62 @@ __global__ __launch_bounds__(64 * SH::W) __attribute__((amdgpu_waves_per_eu(2, 2
 // tile boundaries: the first four stages of the next tile are copied during the
 // last four stages of the current one and land while its epilogue runs.
 //
-// With one wavefront per SIMD nothing else issues while this one waits, so the
-// stage schedule spreads the work between MFMAs: the block barrier for the next
-// stage after the 4th MFMA, one fragment read every 3rd MFMA from the 5th, one
-// copy every 6th MFMA from the 6th. The copies take their source address from
-// scalar registers (the saddr form of global_load_lds_dwordx4, the lane offset in
-// one VGPR), which keeps vector address arithmetic and scalar/vector hazards out
-// of the MFMA stream.
+// With one wavefront per SIMD nothing else issues while this one is busy with
+// anything but an MFMA, and a wavefront issues at most one instruction per
+// four cycles against 16 cycles per MFMA, so the stage schedule keeps at most a
+// few instructions between consecutive MFMAs: the block barrier after the 4th
+// MFMA of every second stage, one fragment read every 3rd MFMA from the 5th,
+// one copy every 6th MFMA from the 6th. A copy is two instructions: an M0
+// write (the LDS address) after one MFMA, and after the next a
+// buffer_load_dwordx4 ... lds whose resource holds the stage's source address
+// and whose scalar offset selects the 16-row block, with the lane offset in one
+// VGPR; the MFMA between them provides the wait state an M0 write needs before
+// an LDS-DMA load.
 //
 // Counter waits: vector-memory operations of a wavefront complete in issue
-// order, so waiting for a stage's copies means allowing only the operations
-// issued after them: the copies of the two later stages (16), plus, in the
-// first three stages of a tile, the 16 stores of the previous tile's epilogue
-// that were issued between them. Requires nks >= kNST - 1 (and even), so the
-// copies never reach beyond the next tile.
+// order, so waiting for some copies means allowing only the operations issued
+// after them. The barrier in stage ks (even) waits for the copies of stages
+// ks + 1 and ks + 2, read in stages ks and ks + 1, allowing those of ks + 3 (8);
+// in a tile's first stage the 16 stores of the previous tile's epilogue sit
+// after them too (24). Before the first tile the prologue issues 16 extra
+// copies (the same bytes as the first stage's own copies, into the same slot)
+// so that the first tile sees the same counts. Requires nks >= kNST - 1 (and
+// even), so the copies never reach beyond the next tile.
 // ---------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
-    static_assert(N == 16 || N == 32, "add the count");
-    if constexpr (N == 16)
+    static_assert(N == 8 || N == 16 || N == 24 || N == 32 || N == 40, "add the count");
+    if constexpr (N == 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 16)
         asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-    else
+    else if constexpr (N == 24)
+        asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+    else if constexpr (N == 32)
         asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(40)\n\ts_barrier" ::: "memory");
+}
+
+// Buffer resource for the copies of one stage (raw, stride 0): base = the
+// stage's first byte in the wave's copy rows (a device address below 2^47,
+// so its high word leaves the stride field zero), nrec bytes from it.
+__device__ __forceinline__ v4i copy_rsrc(uint64_t base, uint32_t nrec) {
+    return (v4i){(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)nrec, 0x00020000};
+}
+
+// M0 = base + c KiB (one SALU instruction; c a constant after unrolling)
+__device__ __forceinline__ void set_m0_kib(uint32_t base, int c) {
+    switch (c) {
+    case 0: asm volatile("s_mov_b32 m0, %0" :: "s"(base) : "memory"); break;
+    case 1: asm volatile("s_add_i32 m0, %0, 0x400" :: "s"(base) : "memory"); break;
+    case 2: asm volatile("s_add_i32 m0, %0, 0x800" :: "s"(base) : "memory"); break;
+    case 3: asm volatile("s_add_i32 m0, %0, 0xc00" :: "s"(base) : "memory"); break;
+    case 4: asm volatile("s_add_i32 m0, %0, 0x1000" :: "s"(base) : "memory"); break;
+    case 5: asm volatile("s_add_i32 m0, %0, 0x1400" :: "s"(base) : "memory"); break;
+    case 6: asm volatile("s_add_i32 m0, %0, 0x1800" :: "s"(base) : "memory"); break;
+    default: asm volatile("s_add_i32 m0, %0, 0x1c00" :: "s"(base) : "memory"); break;
+    }
 }
 
 __global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_persistent(
@@ -1059,9 +1096,9 @@ __global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(
     constexpr int RT = ShapeP::RT, CT = ShapeP::CT, NF = ShapeP::NF, NQ = ShapeP::NQ, FA = ShapeP::FA;
     constexpr int FB = ShapeP::FB, STAGE = ShapeP::STAGE, LPW = ShapeP::LPW, W = ShapeP::W, WN = ShapeP::WN;
     constexpr int TM = ShapeP::TM, TN = ShapeP::TN;
-    constexpr int VMC = (kNST - 3) * LPW;  // copies of the two stages after the one read next
-    constexpr int NSTORE = RT * CT / 4;    // 16-byte stores of one epilogue
+    constexpr int NSTORE = RT * CT / 4;  // 16-byte stores of one epilogue
     constexpr int PRE = 4, RSTEP = 3, CSTEP = 6;
+    static_assert(NSTORE == 2 * LPW, "the prologue's extra copies stand in for one epilogue's stores");
     static_assert(PRE + RSTEP * (NF - 1) < NQ && PRE + 1 + CSTEP * (LPW - 1) < NQ, "schedule fits a stage");
     __shared__ __attribute__((aligned(1024))) int8_t lds[kNST * STAGE];
 
@@ -1071,43 +1108,37 @@ __global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(
     const int lane = threadIdx.x & 63;
     const int wm = wave / WN, wn = wave % WN;
     const int nk = ga.nks;
-    const int64_t row_bytes = (ga.kb / 2) * 1024;  // one 16-row block over all of K
+    const int64_t row_bytes = (ga.kb / 2) * 1024;
     const bool copies_a = wave < W / 2;
     const int wq = wave % (W / 2);
-    // wave-uniform source of this wave's copies for tile b at stage 0 of the launch
-    auto source = [&](int b, int &l, int &tm, int &tn) -> const int8_t * {
+    // q * row_bytes < 2^32 (the launcher checks it)
+    const uint32_t rb32 = (uint32_t)row_bytes;
+    const uint32_t nrec = (uint32_t)(LPW - 1) * rb32 + 1024u;
+    auto source = [&](int b, int &l, int &tm, int &tn) -> uint64_t {
         decode_block(b, total, ga.tiles_m, ga.tiles_n, l, tm, tn);
-        return (copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * FA + wq * LPW) * row_bytes
-                         : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * FB + wq * LPW) * row_bytes) +
-               ga.ks0 * 1024;
+        return (uint64_t)(uintptr_t)((copies_a ? ga.RA + (int64_t)l * ga.planeA + ((int64_t)tm * FA + wq * LPW) * row_bytes
+                                               : ga.RB + (int64_t)l * ga.planeB + ((int64_t)tn * FB + wq * LPW) * row_bytes) +
+                                     ga.ks0 * 1024);
     };
-    __attribute__((address_space(3))) int8_t *lds3 = (__attribute__((address_space(3))) int8_t *)lds;
     const uint32_t lane_off = (uint32_t)lane * 16u;
-    // copy q of a stage: 1 KiB from src + q * row_bytes + lane * 16 into ring slot `slot`
-    auto dma = [&](const int8_t *src, int slot, int q) {
-        const uint64_t a = (uint64_t)(uintptr_t)(src + q * row_bytes);
-        const uint32_t dst = (uint32_t)(uintptr_t)(lds3 + slot * STAGE + (wave * LPW + q) * 1024);
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                     :: "v"(lane_off), "s"(a), "s"(dst) : "memory", "m0");
-    };
+    // LDS byte address of this wave's first copy slot; taken from the array's
+    // address so the compiler sees the copies (inline asm) may write it
+    const uint32_t wave_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) int8_t *)lds) +
+                              (uint32_t)(wave * LPW * 1024);
     auto frag = [&](const int8_t *st, int r) {
         return *(const v4i *)(st + (r < RT ? wm * RT + r : FA + wn * CT + (r - RT)) * 1024 + lane * 16);
     };
 
     int bid = blockIdx.x;
     int l, tm, tn, nl = 0, ntm = 0, ntn = 0;
-    const int8_t *cur = source(bid, l, tm, tn);
+    uint64_t cur = source(bid, l, tm, tn);
     int nbid = bid + G;
-    const int8_t *nxt = nbid < total ? source(nbid, nl, ntm, ntn) : cur;
-    // source of the copies issued during stage ks: stage ks + kNST - 1 of this
-    // tile or of the next; past the last tile, a copy of this tile's last stage
-    // into a slot that is never read (keeps the counter waits constant)
-    auto copy_src = [&](int ks) -> const int8_t * {
-        const int t = ks + kNST - 1;
-        if (t < nk) return cur + t * 1024;
-        if (nbid < total) return nxt + (t - nk) * 1024;
-        return cur + (nk - 1) * 1024;
-    };
+    uint64_t nxt = nbid < total ? source(nbid, nl, ntm, ntn) : cur;
+    // copies issued in stage ks read stage t = ks + kNST - 1 of this tile, or
+    // stage t - nk of the next one (tail = the next tile, or this one again
+    // after the last tile: an in-bounds copy into a slot that is never read)
+    uint64_t tail = nxt;
+    uint64_t src = kNST - 1 < nk ? cur + (kNST - 1) * 1024 : tail;
 
     v4i acc[RT][CT];
 #pragma unroll
@@ -1115,63 +1146,83 @@ __global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int j = 0; j < CT; ++j) acc[i][j] = (v4i){0, 0, 0, 0};
 #pragma unroll
-    for (int st = 0; st < kNST - 1; ++st)
+    for (int st = 0; st < kNST - 1; ++st) {
+        const v4i rs = copy_rsrc(cur + st * 1024, nrec);
 #pragma unroll
-        for (int q = 0; q < LPW; ++q) dma(cur + st * 1024, st, q);
-    vm_wait_barrier<VMC>();  // stages 0 and 1 landed
-    v4i f0[NF], f1[NF];      // fragments of the current / next stage: A tiles, then B tiles
+        for (int q = 0; q < LPW; ++q)
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                         :: "v"(lane_off), "s"(rs), "s"((uint32_t)(st * STAGE) + wave_lds + q * 1024u),
+                            "s"(q * rb32) : "memory");
+    }
+    {
+        const v4i rs = copy_rsrc(src, nrec);  // the first stage's own copies, issued twice more
+#pragma unroll
+        for (int q = 0; q < NSTORE; ++q)
+            asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+                         :: "v"(lane_off), "s"(rs), "s"((uint32_t)((kNST - 1) * STAGE) + wave_lds + (q % LPW) * 1024u),
+                            "s"((q % LPW) * rb32) : "memory");
+    }
+    vm_wait_barrier<3 * LPW + NSTORE>();  // stage 0 landed
+    v4i f0[NF], f1[NF];
 #pragma unroll
     for (int r = 0; r < NF; ++r) f0[r] = frag(lds, r);
 
-    int slot = 0;  // ring slot of the current stage
-    // stage ks: MFMAs on fc; after the barrier, reads of the next stage into fn
-    // (B fragments first) and the copies for stage ks + kNST - 1 into the slot
-    // the previous stage used. after_epi: the previous epilogue's stores were
-    // issued after the copies this stage waits for.
-    auto stage = [&](int ks, v4i(&fc)[NF], v4i(&fn)[NF], bool after_epi) {
-        const int nslot = slot == kNST - 1 ? 0 : slot + 1;
-        const int cslot = slot == 0 ? kNST - 1 : slot - 1;
-        const int8_t *next = lds + nslot * STAGE;
-        const int8_t *src = copy_src(ks);
+    uint32_t rd_off = STAGE;                  // slot read during this stage (that of stage ks + 1)
+    uint32_t cp_off = (kNST - 1) * STAGE;     // slot the copies of this stage fill
+    // stage ks: MFMAs on fc, reads of the next stage into fn (B fragments
+    // first), copies for stage ks + kNST - 1; WAIT: the counter value of the
+    // stage's barrier, 0 for a stage without one
+    auto stage = [&](auto wait, int ks, v4i(&fc)[NF], v4i(&fn)[NF]) {
+        const int8_t *next = lds + rd_off;
+        const v4i rs = copy_rsrc(src, nrec);
+        const uint32_t cbase = cp_off + wave_lds;
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             acc[q / CT][q % CT] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fc[q / CT], fc[RT + q % CT],
                                                                        acc[q / CT][q % CT], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
             if (q == PRE - 1) {
-                if (after_epi)
-                    vm_wait_barrier<VMC + NSTORE>();
-                else
-                    vm_wait_barrier<VMC>();
+                if constexpr (decltype(wait)::value > 0) vm_wait_barrier<decltype(wait)::value>();
             }
             if (q >= PRE && (q - PRE) % RSTEP == 0 && (q - PRE) / RSTEP < NF) {
                 const int i = (q - PRE) / RSTEP;
                 const int r = i < CT ? RT + i : i - CT;
                 fn[r] = frag(next, r);
             }
-            if (q > PRE && (q - PRE - 1) % CSTEP == 0 && (q - PRE - 1) / CSTEP < LPW)
-                dma(src, cslot, (q - PRE - 1) / CSTEP);
+            // copy c: M0 set after MFMA PRE + CSTEP c, the load one MFMA later
+            // (the MFMA between provides the wait state the M0 write needs)
+            if (q >= PRE && (q - PRE) % CSTEP == 0 && (q - PRE) / CSTEP < LPW) set_m0_kib(cbase, (q - PRE) / CSTEP);
+            if (q == PRE + 1)
+                asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(lane_off), "s"(rs) : "memory");
+            else if (q > PRE + 1 && (q - PRE - 1) % CSTEP == 0 && (q - PRE - 1) / CSTEP < LPW)
+                asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                             :: "v"(lane_off), "s"(rs), "s"((uint32_t)((q - PRE - 1) / CSTEP) * rb32) : "memory");
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        slot = nslot;
+        // the next stage's slots and copy source
+        rd_off = rd_off == (kNST - 1) * STAGE ? 0u : rd_off + STAGE;
+        cp_off = cp_off == (kNST - 1) * STAGE ? 0u : cp_off + STAGE;
+        src = ks + kNST == nk ? tail : src + 1024;
     };
 
-    bool after_epi = false;
+    // a block barrier every second stage: the one in stage ks (even) waits for
+    // stages ks + 1 and ks + 2 (read in stages ks and ks + 1), and orders every
+    // read of the slots the copies of stages ks and ks + 1 refill before them
+    const std::integral_constant<int, LPW + NSTORE> first;  // stage 3's copies and NSTORE more after stage 2's
+    const std::integral_constant<int, LPW> even;
+    const std::integral_constant<int, 0> odd;
     while (true) {
-        stage(0, f0, f1, after_epi);
-        stage(1, f1, f0, after_epi);
-        stage(2, f0, f1, after_epi);
-        stage(3, f1, f0, false);
-        for (int ks = 4; ks < nk; ks += 2) {
-            stage(ks, f0, f1, false);
-            stage(ks + 1, f1, f0, false);
+        stage(first, 0, f0, f1);
+        stage(odd, 1, f1, f0);
+        for (int ks = 2; ks < nk; ks += 2) {
+            stage(even, ks, f0, f1);
+            stage(odd, ks + 1, f1, f0);
         }
         const int row0 = tm * TM + wm * RT * 16, col0 = tn * TN + wn * CT * 16;
         store_mod_tiles<RT, CT, true>(acc, (int)mc.p[l / ga.group], mc.pinv[l / ga.group],
                                       ga.planes + (int64_t)l * ga.plane_elems, ga.m_pad, row0, col0, lane,
                                       ga.accumulate != 0);
-        after_epi = true;
 #pragma unroll
         for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -1184,8 +1235,10 @@ __global__ __launch_bounds__(64 * ShapeP::W) __attribute__((amdgpu_waves_per_eu(
         tn = ntn;
         nbid = bid + G;
         if (nbid < total) nxt = source(nbid, nl, ntm, ntn);
+        tail = nxt;
+        src = kNST - 1 < nk ? cur + (kNST - 1) * 1024 : tail;
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing copies before the block ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -1905,10 +1958,11 @@ static bool use_small_tiles(const Layout &L, int planes) {
 }
 
 // The 256 x 256 tile runs on the persistent kernel when a launch has at least
-// kNST - 1 stages (and m_pad < 2^27, for its 32-bit lane offsets);
-// OZ2_GEMM_KERNEL=blocks forces the one-tile-per-block kernel.
-static bool use_persistent(int nks, int64_t m_pad) {
-    if (nks < kNST - 1 || m_pad >= ((int64_t)1 << 27)) return false;
+// kNST - 1 stages, m_pad < 2^27 (its 32-bit store offsets) and k_pad < 2^25
+// (its 32-bit copy offsets, 7 x 16 k_pad); OZ2_GEMM_KERNEL=blocks forces the
+// one-tile-per-block kernel.
+static bool use_persistent(int nks, const Layout &L) {
+    if (nks < kNST - 1 || L.m_pad >= ((int64_t)1 << 27) || L.k_pad >= ((int64_t)1 << 25)) return false;
     const char *force = getenv("OZ2_GEMM_KERNEL");
     return !(force && strcmp(force, "blocks") == 0);
 }
@@ -1950,7 +2004,7 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
         if (small) {
             auto kern = k_gemm<EPI_MOD, ShapeS>;
             OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
-        } else if (use_persistent(g.nks, L.m_pad)) {
+        } else if (use_persistent(g.nks, L)) {
             // one block per compute unit (the kernel's 160 KiB of LDS admits no second)
             const int grid = blocks < compute_units() ? blocks : compute_units();
             OZ2_LAUNCH(e, k_gemm_persistent, dim3(grid), dim3(64 * ShapeP::W), 0, s, g, mc);
