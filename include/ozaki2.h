@@ -49,7 +49,9 @@
  * always use two. OZ2_GEMM_KERNEL=blocks runs the 256 x 256 tile one tile per
  * block (eight wavefronts) instead of on the default persistent kernel (one
  * block of four wavefronts per compute unit walking its tiles). Results do not
- * depend on any of these settings.
+ * depend on any of these settings. OZ2_CRT=fma reconstructs real products
+ * with 17 to 20 moduli with FP64 FMAs on 40-bit pieces instead of digit sums
+ * on the matrix cores (the same results).
  *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by

@@ -14,6 +14,7 @@ namespace oz2 {
 
 constexpr int kMaxModuli = 20;
 constexpr int kChunks = 4;          // CRT weights and P in 40-bit pieces (4 x 40 >= 156 bits)
+constexpr int kChunks32 = 5;        // P in 32-bit pieces (5 x 32 >= 156 bits)
 constexpr int kChunkBits = 40;
 constexpr int kMaxDigits = 20;      // W_l < P < 2^156 has at most 20 signed base-256 digits
 constexpr int kExpNonfinite = INT32_MIN;  // exponent marker: row/column holds Inf or NaN
@@ -44,8 +45,9 @@ struct CrtConsts {
     double P[kChunks];              // P, 40-bit pieces
     double H[kChunks];              // P / 2, 40-bit pieces
     double pinv120;                 // RN(2^120 / P)
-    double P32[kChunks];            // P in 32-bit pieces (used for P < 2^128)
-    double H32[kChunks];            // P / 2 in 32-bit pieces
+    double P32[kChunks32];          // P in 32-bit pieces
+    double H32[kChunks32];          // P / 2 in 32-bit pieces
+    double pinv128;                 // RN(2^128 / P)
     double pinv96;                  // RN(2^96 / P)
     double pinv64;                  // RN(2^64 / P)
     double pinv32;                  // RN(2^32 / P)

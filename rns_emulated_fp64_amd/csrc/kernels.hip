@@ -1372,7 +1372,7 @@ __device__ __forceinline__ double limbs_to_double(const double x[4], int scale_d
     return ldexp((double)mant, scale - lz + 11 - scale_down);
 }
 
-// The same for a normalized non-negative vector of NP (2..4) 32-bit pieces
+// The same for a normalized non-negative vector of NP (2..5) 32-bit pieces
 // (x[t] in [0, 2^32)): the top 64 bits of the integer with the bits below
 // OR-ed into the last place (round to odd) convert to double with a single
 // rounding, which then equals the rounding of the whole integer (64 >= 53 + 2
@@ -1382,10 +1382,16 @@ __device__ __forceinline__ double limbs32_to_double(const double x[NP], int scal
     const uint64_t w0 = ((uint64_t)(uint32_t)x[1] << 32) | (uint32_t)x[0];
     const uint64_t w1 = NP < 3 ? 0 : ((NP > 3 ? (uint64_t)(uint32_t)x[NP > 3 ? 3 : 0] << 32 : 0) |
                                       (uint32_t)x[NP > 2 ? 2 : 0]);
+    const uint64_t w2 = NP > 4 ? (uint64_t)(uint32_t)x[NP > 4 ? 4 : 0] : 0;
     uint64_t top;
     int scale;
     bool odd;
-    if (w1 != 0) {
+    if (w2 != 0) {
+        const int lz = __clzll(w2);
+        top = (w2 << lz) | ((w1 >> 1) >> (63 - lz));
+        odd = ((w1 << lz) | w0) != 0;
+        scale = 128 - lz;
+    } else if (w1 != 0) {
         const int lz = __clzll(w1);
         top = (w1 << lz) | ((w0 >> 1) >> (63 - lz));
         odd = (w0 << lz) != 0;
@@ -1417,15 +1423,19 @@ __device__ __forceinline__ OutT crt_finish(const double S[4], int ei, int fj, co
     return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
 
-// As crt_finish for S in NP (2..4) 32-bit pieces, enough for the digit sums
-// and for P (P < 2^(32 NP), at most 16 moduli). The quotient estimate uses
-// S / 2^(32 (NP - 1)) and RN(2^(32 (NP - 1)) / P).
+// As crt_finish for S in NP (2..5) 32-bit pieces, enough for the digit sums
+// and for P (P < 2^(32 NP)). The quotient estimate uses S / 2^(32 (NP - 1))
+// and RN(2^(32 (NP - 1)) / P).
 template <class OutT, int NP = 4>
 __device__ __forceinline__ OutT crt_finish32(const double S[NP], int ei, int fj, const CrtConsts &cc) {
     double top = S[NP - 1];
+    double sc = 1.0;
 #pragma unroll
-    for (int t = NP - 2; t >= 0; --t) top = fma(S[t], 0x1p-32 * (t == NP - 2 ? 1.0 : t == NP - 3 ? 0x1p-32 : 0x1p-64), top);
-    const double pinv = NP == 4 ? cc.pinv96 : NP == 3 ? cc.pinv64 : cc.pinv32;
+    for (int t = NP - 2; t >= 0; --t) {
+        sc *= 0x1p-32;
+        top = fma(S[t], sc, top);
+    }
+    const double pinv = NP == 5 ? cc.pinv128 : NP == 4 ? cc.pinv96 : NP == 3 ? cc.pinv64 : cc.pinv32;
     double x[NP], sg;
     crt_lift<32, NP>(S, x, sg, top, cc.P32, cc.H32, pinv);
     const double mag = limbs32_to_double<sizeof(OutT) == 4, NP>(x, ei + fj);
@@ -1536,6 +1546,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
             for (int t = 0; t < NP; ++t) {
                 const int lo = D[4 * t] + D[4 * t + 1] * 256, hi = D[4 * t + 2] + D[4 * t + 3] * 256;
                 S[t] = fma((double)hi, 65536.0, (double)lo);
+            }
+            const int64_t i = i0 + u;
+            out[u] = i < m ? crt_finish32<OutT, NP>(S, e[i], fj, cc) : (OutT)0;
+        }
+        store_run_nt(C + i0 + j * ldc, out, m - i0);
+    }
+}
+
+// 17..20 moduli on the matrix cores: the weights have up to 20 signed
+// base-256 digits and P < 2^160 (five 32-bit pieces). The layout is
+// k_crt_mma's, extended by a second B operand per entry holding moduli 16..19
+// in its first four bytes (zeros after) and a second digit block whose rows
+// hold digit 16 + v in register v (v < 4): per group of 64 entries, four
+// MFMAs accumulate D0 (digits 0..15) and D1 (digits 16..19) over all the
+// moduli. |D_v| <= 20 * 128 * 128 < 2^18.4, so the five 32-bit pieces stay
+// exact (|piece| < 2^42.5) for crt_finish32.
+template <class OutT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_crt_mma20(
+    const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
+    const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
+    constexpr int NP = 5;
+    __shared__ __attribute__((aligned(16))) int8_t digit[kMaxDigits][32];
+    if (threadIdx.x < kMaxDigits * 8) {
+        const int v = threadIdx.x >> 3, b4 = (threadIdx.x & 7) * 4;
+        *(uint32_t *)&digit[v][b4] = *(const uint32_t *)&cc.digit[v][b4];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 31;
+    const bool mine = ((r >> 2) & 1) == (lane >> 5);
+    const int dv = 4 * (r >> 3) + (r & 3);  // the digit this lane's accumulator row carries
+    const v4i zero = {0, 0, 0, 0};
+    const v4i a_lo0 = mine ? *(const v4i *)&digit[dv][0] : zero;
+    const v4i a_hi0 = mine ? (v4i){*(const int *)&digit[dv][16], 0, 0, 0} : zero;
+    const v4i a_lo1 = mine && dv < 4 ? *(const v4i *)&digit[16 + (dv & 3)][0] : zero;
+    const v4i a_hi1 = mine && dv < 4 ? (v4i){*(const int *)&digit[16 + (dv & 3)][16], 0, 0, 0} : zero;
+
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i0;
+        uint32_t w[20];
+#pragma unroll
+        for (int l = 0; l < 20; ++l) w[l] = l < cc.n ? *(const uint32_t *)(src + (int64_t)l * plane_elems) : 0u;
+        // 4 x 4 byte transposes: R[u] = residues of row i0 + u, moduli 0..15;
+        // H[u] = moduli 16..19
+        v4i R[4];
+        uint32_t H[4];
+#pragma unroll
+        for (int g = 0; g < 5; ++g) {
+            const uint32_t a0 = w[4 * g], a1 = w[4 * g + 1], a2 = w[4 * g + 2], a3 = w[4 * g + 3];
+            const uint32_t t01l = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // a0.0 a1.0 a0.1 a1.1
+            const uint32_t t01h = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // a0.2 a1.2 a0.3 a1.3
+            const uint32_t t23l = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+            const uint32_t t23h = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+            const uint32_t q0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+            const uint32_t q1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+            const uint32_t q2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+            const uint32_t q3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+            if (g < 4) {
+                R[0][g] = (int)q0;
+                R[1][g] = (int)q1;
+                R[2][g] = (int)q2;
+                R[3][g] = (int)q3;
+            } else {
+                H[0] = q0;
+                H[1] = q1;
+                H[2] = q2;
+                H[3] = q3;
+            }
+        }
+        const int fj = f[j];
+        OutT out[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const v4i Bh = {(int)H[u], 0, 0, 0};
+            v16i D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_lo0, R[u], (v16i){0}, 0, 0, 0);
+            D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_hi0, Bh, D0, 0, 0, 0);
+            v16i D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_lo1, R[u], (v16i){0}, 0, 0, 0);
+            D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_hi1, Bh, D1, 0, 0, 0);
+            double S[NP];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int lo = D0[4 * t] + D0[4 * t + 1] * 256, hi = D0[4 * t + 2] + D0[4 * t + 3] * 256;
+                S[t] = fma((double)hi, 65536.0, (double)lo);
+            }
+            {
+                const int lo = D1[0] + D1[1] * 256, hi = D1[2] + D1[3] * 256;
+                S[4] = fma((double)hi, 65536.0, (double)lo);
             }
             const int64_t i = i0 + u;
             out[u] = i < m ? crt_finish32<OutT, NP>(S, e[i], fj, cc) : (OutT)0;
@@ -2061,9 +2159,11 @@ static hipError_t launch_crt_t(const int8_t *planes, int64_t m, int64_t n, const
     if (cc.n <= 16 && cc.nd <= 16 && cc.np32 <= 4) {
         auto kern = cc.np32 == 2 ? k_crt_mma<OutT, 2> : cc.np32 == 3 ? k_crt_mma<OutT, 3> : k_crt_mma<OutT, 4>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
+    } else if (cc.n <= 20 && cc.nd <= 20 && cc.np32 <= 5 && !(getenv("OZ2_CRT") && strcmp(getenv("OZ2_CRT"), "fma") == 0)) {
+        auto kern = k_crt_mma20<OutT>;
+        OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     } else {
-        // 17..20 moduli: the 2 x 2 MFMA blocks are mostly padding there, and
-        // the FMA form measures slightly faster on MI355X
+        // FP64-FMA form on 40-bit pieces (OZ2_CRT=fma)
         auto kern = k_crt<OutT>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     }

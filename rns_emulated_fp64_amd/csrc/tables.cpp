@@ -194,6 +194,7 @@ void build(Tables &t, int n) {
     long double Pld = 0.0L;
     for (int i = 7; i >= 0; --i) Pld = Pld * 4294967296.0L + (long double)P.d[i];
     t.crt.pinv120 = (double)(ldexpl(1.0L, 120) / Pld);
+    t.crt.pinv128 = (double)(ldexpl(1.0L, 128) / Pld);
     t.crt.pinv96 = (double)(ldexpl(1.0L, 96) / Pld);
     t.crt.pinv64 = (double)(ldexpl(1.0L, 64) / Pld);
     t.crt.pinv32 = (double)(ldexpl(1.0L, 32) / Pld);
@@ -202,7 +203,7 @@ void build(Tables &t, int n) {
         t.crt.np32 = by_digits > by_p ? by_digits : by_p;
         if (t.crt.np32 < 2) t.crt.np32 = 2;
     }
-    for (int c = 0; c < kChunks; ++c) {  // 32-bit pieces (the low 128 bits)
+    for (int c = 0; c < kChunks32; ++c) {  // 32-bit pieces (P < 2^160)
         t.crt.P32[c] = (double)P.d[c];
         t.crt.H32[c] = (double)H.d[c];
     }

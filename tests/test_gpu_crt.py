@@ -71,6 +71,18 @@ def crafted_case(N: int, seed: int):
 
 @pytest.mark.parametrize("N", [2, 3, 8, 14, 15, 16, 17, 18, 20])
 def test_crt_edges_bitwise(N):
+    _crt_edges(N)
+
+
+@pytest.mark.parametrize("N", [17, 18, 19, 20])
+def test_crt_edges_bitwise_fma_form(monkeypatch, N):
+    # 17..20 moduli run on the matrix cores by default; OZ2_CRT=fma keeps the
+    # FP64-FMA form on 40-bit pieces, which must agree on the same edges
+    monkeypatch.setenv("OZ2_CRT", "fma")
+    _crt_edges(N)
+
+
+def _crt_edges(N):
     moduli, P, X, e, f = crafted_case(N, 1000 + N)
     m, n = X.shape
     c = np.empty((N, n, m), dtype=np.uint8)  # [l][j][i], values in [0, p_l)
