@@ -1562,7 +1562,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
 // MFMAs accumulate D0 (digits 0..15) and D1 (digits 16..19) over all the
 // moduli. |D_v| <= 20 * 128 * 128 < 2^18.4, so the five 32-bit pieces stay
 // exact (|piece| < 2^42.5) for crt_finish32.
-template <class OutT>
+template <class OutT, int NM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_crt_mma20(
     const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
     const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
@@ -1588,7 +1588,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         const int8_t *src = planes + j * m_pad + i0;
         uint32_t w[20];
 #pragma unroll
-        for (int l = 0; l < 20; ++l) w[l] = l < cc.n ? *(const uint32_t *)(src + (int64_t)l * plane_elems) : 0u;
+        for (int l = 0; l < 20; ++l) w[l] = l < NM ? *(const uint32_t *)(src + (int64_t)l * plane_elems) : 0u;
         // 4 x 4 byte transposes: R[u] = residues of row i0 + u, moduli 0..15;
         // H[u] = moduli 16..19
         v4i R[4];
@@ -2159,8 +2159,10 @@ static hipError_t launch_crt_t(const int8_t *planes, int64_t m, int64_t n, const
     if (cc.n <= 16 && cc.nd <= 16 && cc.np32 <= 4) {
         auto kern = cc.np32 == 2 ? k_crt_mma<OutT, 2> : cc.np32 == 3 ? k_crt_mma<OutT, 3> : k_crt_mma<OutT, 4>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
-    } else if (cc.n <= 20 && cc.nd <= 20 && cc.np32 <= 5 && !(getenv("OZ2_CRT") && strcmp(getenv("OZ2_CRT"), "fma") == 0)) {
-        auto kern = k_crt_mma20<OutT>;
+    } else if (cc.n >= 17 && cc.n <= 20 && cc.nd <= 20 && cc.np32 <= 5 &&
+               !(getenv("OZ2_CRT") && strcmp(getenv("OZ2_CRT"), "fma") == 0)) {
+        auto kern = cc.n == 17 ? k_crt_mma20<OutT, 17> : cc.n == 18 ? k_crt_mma20<OutT, 18>
+                  : cc.n == 19 ? k_crt_mma20<OutT, 19> : k_crt_mma20<OutT, 20>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, C, ldc);
     } else {
         // FP64-FMA form on 40-bit pieces (OZ2_CRT=fma)
