@@ -69,7 +69,7 @@ def crafted_case(N: int, seed: int):
     return moduli, P, X, e, f
 
 
-@pytest.mark.parametrize("N", [2, 3, 8, 14, 15, 16, 17, 18, 20])
+@pytest.mark.parametrize("N", [2, 3, 8, 14, 15, 16, 17, 18, 19, 20])
 def test_crt_edges_bitwise(N):
     _crt_edges(N)
 
