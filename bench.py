@@ -54,9 +54,10 @@ def parse():
 
 
 def gemm_source_hash():
-    """SHA-256 of the GEMM's source (its section of kernels.hip and common.h)
-    with comments and blank lines removed: it changes when the code does, not
-    when only its comments do."""
+    """SHA-256 of the GEMM's source with comments and blank lines removed: the
+    GEMM section of kernels.hip, its launcher (tile shape and kernel choice,
+    grid), and the tiling constants and ModConsts / Layout structs of common.h.
+    It changes when that code does, not when only comments or other kernels do."""
     import hashlib
     import re
 
@@ -67,8 +68,11 @@ def gemm_source_hash():
 
     src = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "kernels.hip")).read()
     sec = src[src.index("// Step 3: INT8 GEMM"):src.index("// Steps 4 + 5")]
+    launch = src[src.index("static int compute_units()"):src.index("hipError_t launch_gemm_raw(")]
     common = open(os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "common.h")).read()
-    return hashlib.sha256((code(sec) + "\n" + code(common)).encode()).hexdigest()
+    parts = re.findall(r"constexpr int k(?:TileM|TileN|KPad) = \d+;", common)
+    parts += re.findall(r"struct (?:ModConsts|Layout) \{.*?\};", common, flags=re.S)
+    return hashlib.sha256("\n".join(code(x) for x in [sec, launch] + parts).encode()).hexdigest()
 
 
 def gemm_kernel_name():
