@@ -43,6 +43,7 @@ SHAPES = [
     (700, 530, 390, 20),     # 3 x 3 x 20 = 180 tiles
     (1100, 1100, 300, 11),   # 5 x 5 x 11 = 275 tiles: 19 blocks walk a second tile
     (1024, 1024, 1000, 20),  # 320 tiles, 16 stages
+    (1500, 1500, 256, 16),   # 6 x 6 x 16 = 576 tiles: two or three per block, four stages each
 ]
 
 
@@ -64,11 +65,11 @@ def test_persistent_walking_tiles_against_oracle():
     full_parity(A, B, 17, want_prod=False)
 
 
-def test_persistent_split_inner_dimension(monkeypatch):
-    # k_pad = 65536 + 384: launches of 1024 and 6 stages; the second one adds
-    # to the residues of the first (the accumulating epilogue) and is still
-    # long enough for the persistent kernel
-    k = 65536 + 300
+@pytest.mark.parametrize("k", [65536 + 300, 65536 + 200])
+def test_persistent_split_inner_dimension(monkeypatch, k):
+    # k_pad = 65536 + 384 (65536 + 256): launches of 1024 and 6 (4) stages;
+    # the second one adds to the residues of the first (the accumulating
+    # epilogue) and is still long enough for the persistent kernel
     A, B = W.spread_case(260, 40, k, 0.5, seed=3)
     g = _both_kernels(monkeypatch, A, B, 8)
     assert_bitwise_equal(g["C"], O.os2_dgemm(A, B, 8)["C"], "C against the oracle")
