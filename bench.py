@@ -77,7 +77,8 @@ def gemm_source_hash():
 
 def gemm_kernel_name():
     """The INT8 GEMM kernel the headline workload runs on (256 x 256 tiles, more
-    than four 64-deep stages): the persistent one unless OZ2_GEMM_KERNEL=blocks."""
+    tiles than compute units, more than four 64-deep stages): the persistent one
+    unless OZ2_GEMM_KERNEL=blocks."""
     return "k_gemm<EPI_MOD>" if os.environ.get("OZ2_GEMM_KERNEL") == "blocks" else "k_gemm_persistent"
 
 

@@ -46,10 +46,11 @@
  * GEMM writing residue planes and a reconstruction reading them); by default
  * one launch only for tiny products (N times the stages of 64 of k at most
  * 16, at most 64 tiles of 64 x 64), two otherwise; the debug entry points
- * always use two. OZ2_GEMM_KERNEL=blocks runs the 256 x 256 tile one tile per
- * block (eight wavefronts) instead of on the default persistent kernel (one
- * block of four wavefronts per compute unit walking its tiles). Results do not
- * depend on any of these settings. OZ2_CRT=fma reconstructs real products
+ * always use two. The 256 x 256 tile runs on a persistent kernel (one block of
+ * four wavefronts per compute unit walking its tiles) when there are more
+ * tiles than compute units, else one tile per block (eight wavefronts);
+ * OZ2_GEMM_KERNEL=blocks or =persistent forces either. Results do not depend
+ * on any of these settings. OZ2_CRT=fma reconstructs real products
  * with 17 to 20 moduli with FP64 FMAs on 40-bit pieces instead of digit sums
  * on the matrix cores (the same results).
  *

@@ -2055,14 +2055,19 @@ static bool use_small_tiles(const Layout &L, int planes) {
     return 2 * blocks <= (int64_t)compute_units();
 }
 
-// The 256 x 256 tile runs on the persistent kernel when a launch has at least
+// The 256 x 256 tile runs on the persistent kernel when there are more tiles
+// than compute units (with at most one tile per block it only adds the
+// one-wave kernel's exposed prologue and epilogue) and the launch has at least
 // kNST - 1 stages, m_pad < 2^27 (its 32-bit store offsets) and k_pad < 2^25
-// (its 32-bit copy offsets, 7 x 16 k_pad); OZ2_GEMM_KERNEL=blocks forces the
-// one-tile-per-block kernel.
-static bool use_persistent(int nks, const Layout &L) {
+// (its 32-bit copy offsets, 7 x 16 k_pad). OZ2_GEMM_KERNEL=blocks or
+// =persistent forces either kernel (the latter within those limits).
+static bool use_persistent(int nks, const Layout &L, int blocks) {
     if (nks < kNST - 1 || L.m_pad >= ((int64_t)1 << 27) || L.k_pad >= ((int64_t)1 << 25)) return false;
-    const char *force = getenv("OZ2_GEMM_KERNEL");
-    return !(force && strcmp(force, "blocks") == 0);
+    if (const char *force = getenv("OZ2_GEMM_KERNEL")) {
+        if (strcmp(force, "blocks") == 0) return false;
+        if (strcmp(force, "persistent") == 0) return true;
+    }
+    return blocks > compute_units();
 }
 
 static GemmArgs gemm_args(const int8_t *RA, const int8_t *RB, int nmod, int group, const Layout &L, bool small) {
@@ -2102,7 +2107,7 @@ hipError_t launch_gemm_mod(const int8_t *RA, const int8_t *RB, int nmod, int gro
         if (small) {
             auto kern = k_gemm<EPI_MOD, ShapeS>;
             OZ2_LAUNCH(e, kern, dim3(blocks), dim3(64 * ShapeS::W), 0, s, g, mc);
-        } else if (use_persistent(g.nks, L)) {
+        } else if (use_persistent(g.nks, L, blocks)) {
             // one block per compute unit (the kernel's 160 KiB of LDS admits no second)
             const int grid = blocks < compute_units() ? blocks : compute_units();
             OZ2_LAUNCH(e, k_gemm_persistent, dim3(grid), dim3(64 * ShapeP::W), 0, s, g, mc);

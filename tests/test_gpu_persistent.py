@@ -1,7 +1,8 @@
 """The persistent form of the 256 x 256 INT8 GEMM (one block per compute unit
 walking its tiles, the copy ring running across tile boundaries; the default
-for launches of at least four 64-deep stages) against the one-tile-per-block
-kernel (OZ2_GEMM_KERNEL=blocks) and against the oracle: the reduced residue
+when there are more tiles than compute units and a launch has at least four
+64-deep stages; OZ2_GEMM_KERNEL=persistent forces it) against the
+one-tile-per-block kernel (OZ2_GEMM_KERNEL=blocks) and against the oracle: the reduced residue
 planes and C bit-identical. Shapes cover one tile per block, a grid of more
 tiles than compute units (blocks walking two tiles, a ragged last round), the
 shortest inner dimension it takes (four stages), an inner dimension split into
@@ -29,7 +30,7 @@ def _both_kernels(monkeypatch, A, B, N, mode="fast"):
     monkeypatch.setenv("OZ2_GEMM_TILE", "256")
     monkeypatch.setenv("OZ2_GEMM_KERNEL", "blocks")
     g0 = run_debug(A, B, N, mode, want_prod=False, want_res=False)
-    monkeypatch.delenv("OZ2_GEMM_KERNEL")
+    monkeypatch.setenv("OZ2_GEMM_KERNEL", "persistent")
     g1 = run_debug(A, B, N, mode, want_prod=False, want_res=False)
     assert np.array_equal(g1["red"], g0["red"]), "reduced residue planes differ between the two kernels"
     assert_bitwise_equal(g1["C"], g0["C"], "C (persistent vs blocks)")
@@ -59,10 +60,19 @@ def test_persistent_accurate_mode(monkeypatch):
 
 
 def test_persistent_walking_tiles_against_oracle():
-    # 4 x 4 tiles x 17 moduli = 272 > 256 blocks, so some blocks take a second
-    # tile and its first stages are copied during the first tile's epilogue
+    # 4 x 4 tiles x 17 moduli = 272 > 256 blocks (the persistent kernel by
+    # default), so some blocks take a second tile and its first stages are
+    # copied during the first tile's epilogue
     A, B = W.spread_case(1024, 1024, 300, 1.0, seed=17)
     full_parity(A, B, 17, want_prod=False)
+
+
+def test_persistent_forced_against_oracle(monkeypatch):
+    # fewer tiles than compute units: the block kernel by default, the
+    # persistent one when forced (one tile per block)
+    monkeypatch.setenv("OZ2_GEMM_KERNEL", "persistent")
+    A, B = W.spread_case(700, 530, 390, 1.0, seed=18)
+    full_parity(A, B, 12, want_prod=False)
 
 
 @pytest.mark.parametrize("k", [65536 + 300, 65536 + 200])
@@ -81,7 +91,7 @@ def test_persistent_complex(monkeypatch):
     monkeypatch.setenv("OZ2_GEMM_TILE", "256")
     monkeypatch.setenv("OZ2_GEMM_KERNEL", "blocks")
     g0 = run_complex(A, B, 14, want_prod=False)
-    monkeypatch.delenv("OZ2_GEMM_KERNEL")
+    monkeypatch.setenv("OZ2_GEMM_KERNEL", "persistent")
     g1 = run_complex(A, B, 14, want_prod=False)
     assert np.array_equal(g1["red"], g0["red"]), "reduced planes differ"
     assert_bitwise_equal(g1["C_re"], g0["C_re"], "Re C")

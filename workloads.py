@@ -81,6 +81,10 @@ CONFIGS = {
     "spread1.0_256_n14": dict(m=256, n=256, k=256, num_moduli=14, kind="spread", phi=1.0, seed=0),
     # 2048^3 scale sweep, N=14.
     "scale_sweep_2048_n14": dict(m=2048, n=2048, k=2048, num_moduli=14, kind="sweep", seed=0),
+    # 2048^3 and 8192^3, phi=1.0, N=16: the headline draw at the sizes around it
+    # (a size sweep of the GEMM kernels).
+    "spread1.0_2048_n16": dict(m=2048, n=2048, k=2048, num_moduli=16, kind="spread", phi=1.0, seed=0),
+    "spread1.0_8192_n16": dict(m=8192, n=8192, k=8192, num_moduli=16, kind="spread", phi=1.0, seed=0),
     # 16384^3, phi=1.0, N=18 (2 GiB per operand).
     "spread1.0_16384_n18": dict(m=16384, n=16384, k=16384, num_moduli=18, kind="spread", phi=1.0, seed=0),
     # Single precision ("Improved Scaling ...", section Zentrale Beiträge: the
