@@ -733,9 +733,10 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // limit (it moves less accumulator data per operation). The grid runs over
 // (modulus, tile row, tile column); block ids are remapped so each XCD works
 // through a compact group of tiles of one modulus and its L2 serves the shared
-// A and B panels. Launches of four or more stages run the 256 x 256 tile on the
-// persistent one-wave-per-SIMD kernel further below (k_gemm_persistent), which
-// keeps this kernel's ring, tile order and epilogue.
+// A and B panels. With more 256 x 256 tiles than compute units (and four or
+// more stages per launch) they run on the persistent one-wave-per-SIMD kernel
+// further below (k_gemm_persistent), which keeps this kernel's ring, tile order
+// and epilogue.
 constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
 constexpr int kNST = 5;                    // LDS stages in the ring
 constexpr int kLoadsPerWave = 4;           // 1 KiB copies per wave per stage (both tile shapes)
