@@ -60,6 +60,14 @@ def test_gemm_kernels_do_not_spill(kernels):
         assert r.get("ScratchSize", 0) == 0, (name, r)
 
 
+def test_no_kernel_uses_scratch(kernels):
+    # every kernel of the library (scale, split, GEMMs, reconstructions,
+    # checks) keeps its state in registers and LDS
+    assert len(kernels) > 20, sorted(kernels)
+    for name, r in kernels.items():
+        assert r.get("VGPRs Spill", 0) == 0 and r.get("ScratchSize", 0) == 0, (name, r)
+
+
 def test_persistent_kernel_resources(kernels):
     name = next(k for k in kernels if "k_gemm_persistent" in k)
     r = kernels[name]
