@@ -24,9 +24,15 @@ def setup_module(module):
     oz.lib()
 
 
-@pytest.mark.parametrize("kind,mode,N", [("d", "fast", 16), ("d", "accurate", 14), ("s", "fast", 8)])
-def test_graph_replays_match_eager_calls(kind, mode, N):
-    m, n, k = 300, 260, 700
+@pytest.mark.parametrize("kind,mode,N,shape", [
+    ("d", "fast", 16, (300, 260, 700)),
+    ("d", "accurate", 14, (300, 260, 700)),
+    ("s", "fast", 8, (300, 260, 700)),
+    # 4 x 5 tiles of 256 x 256 x 17 moduli = 340 > 256: the persistent GEMM in the graph
+    ("d", "fast", 17, (1024, 1100, 520)),
+])
+def test_graph_replays_match_eager_calls(kind, mode, N, shape):
+    m, n, k = shape
     single = kind == "s"
     call = oz.ozaki2_sgemm_ws if single else oz.ozaki2_dgemm_ws
     dt = torch.float32 if single else torch.float64
