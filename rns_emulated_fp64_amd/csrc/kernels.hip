@@ -739,7 +739,7 @@ __global__ __launch_bounds__(256) void k_quantize(const T *__restrict__ A, int64
 // and epilogue.
 constexpr int kBK = 64;                    // K bytes per stage (one MFMA k-step)
 constexpr int kNST = 5;                    // LDS stages in the ring
-constexpr int kLoadsPerWave = 4;           // 1 KiB copies per wave per stage (both tile shapes)
+constexpr int kLoadsPerWave = 4;           // 1 KiB copies per wave per stage of k_gemm (both of its shapes)
 constexpr int kGroupM = 4;                 // tile rows per raster group
 constexpr int kReduceStages = 1024;        // stages per launch: 1024 * 64 * 2^14 = 2^30, the range of smod
 // copies a wave may leave in flight at a stage barrier: the kNST - 3 stages
