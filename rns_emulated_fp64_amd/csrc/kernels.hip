@@ -1078,7 +1078,11 @@ __device__ __forceinline__ v4i copy_rsrc(uint64_t base, uint32_t nrec) {
     return (v4i){(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xffffu), (int)nrec, 0x00020000};
 }
 
-// M0 = base + c KiB (one SALU instruction; c a constant after unrolling)
+// M0 = base + c KiB (one SALU instruction; c a constant after unrolling). The
+// copy that uses it is a separate statement one MFMA later; this relies on the
+// compiler not touching M0 in between, which holds in k_gemm_persistent (it
+// has no LDS-DMA builtins, messages or indexed register moves that would make
+// the compiler write M0; the compiled code shows no other M0 writes).
 __device__ __forceinline__ void set_m0_kib(uint32_t base, int c) {
     switch (c) {
     case 0: asm volatile("s_mov_b32 m0, %0" :: "s"(base) : "memory"); break;
