@@ -1,5 +1,6 @@
 """Register and scratch use of the INT8 GEMM kernels, from the compiler's
-resource remarks for gfx950 (a device-only compile, no GPU needed).
+resource remarks for gfx950 (a device-only compile, no GPU needed), and the
+persistent GEMM's M0 discipline in its compiled code.
 
 The GEMM loops keep every accumulator and fragment in registers; a spill
 would put scratch loads into the loop or the epilogue, and a scratch load's
@@ -74,3 +75,34 @@ def test_persistent_kernel_resources(kernels):
     assert r.get("SGPRs Spill", 0) == 0, r
     assert r["LDS Size"] == 5 * 32 * 1024, r  # the five-slot ring of 32 KiB stages
     assert r["Occupancy"] == 1, r             # one wavefront per SIMD by design
+
+
+def test_persistent_kernel_m0_written_only_by_its_copies():
+    # the persistent GEMM sets M0 (the LDS address of a copy) in one inline-asm
+    # statement and issues the copy in the next; that is only sound if the
+    # compiler writes M0 nowhere in the kernel itself
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    src = os.path.join(ROOT, "rns_emulated_fp64_amd", "csrc", "kernels.hip")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off", "-Xclang", "-target-feature",
+           "-Xclang", "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "--cuda-device-only", "-S", src,
+           "-o", "-"]
+    out = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = out.stdout.splitlines()
+    start = next(i for i, l in enumerate(lines) if re.match(r"^_ZN3oz217k_gemm_persistent\S*:", l))
+    end = next(i for i in range(start, len(lines)) if "s_endpgm" in lines[i])
+    in_asm, asm_writes, other = False, 0, []
+    for l in lines[start:end]:
+        t = l.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+        elif t.startswith(";;#ASMEND"):
+            in_asm = False
+        elif re.match(r"^s_\w+\s+m0\b", t):
+            if in_asm:
+                asm_writes += 1
+            else:
+                other.append(t)
+    assert asm_writes >= 8, asm_writes
+    assert not other, other
