@@ -1501,8 +1501,11 @@ __global__ __launch_bounds__(256) void k_crt(const int8_t *__restrict__ planes, 
 // its own entry, digit v in register v. S is then assembled from the D_v into
 // NP exact 32-bit pieces (|piece| < 2^42.1) for crt_finish32; NP = 2 or 3
 // when the weights and P are short (few moduli), which shortens the lift.
+// The row exponents are loaded once, ahead of the column loop. The occupancy
+// hint of 7 gives the scalar registers that needs without a vector spill, and
+// the 64 VGPRs still allow 8 waves per SIMD.
 template <class OutT, int NP = 4>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_crt_mma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7))) void k_crt_mma(
     const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
     const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
     __shared__ __attribute__((aligned(16))) int8_t digit[16][16];
@@ -1520,6 +1523,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
     // the MFMAs always run on full wavefronts
     const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    int ei[4];  // the row exponents, the same for every column
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ei[u] = i0 + u < m ? e[i0 + u] : 0;
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
         const int8_t *src = planes + j * m_pad + i0;
         uint32_t w[16];
@@ -1553,7 +1559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k
                 S[t] = fma((double)hi, 65536.0, (double)lo);
             }
             const int64_t i = i0 + u;
-            out[u] = i < m ? crt_finish32<OutT, NP>(S, e[i], fj, cc) : (OutT)0;
+            out[u] = i < m ? crt_finish32<OutT, NP>(S, ei[u], fj, cc) : (OutT)0;
         }
         store_run_nt(C + i0 + j * ldc, out, m - i0);
     }
@@ -1589,6 +1595,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 
     const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    int ei[4];  // the row exponents, the same for every column
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ei[u] = i0 + u < m ? e[i0 + u] : 0;
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
         const int8_t *src = planes + j * m_pad + i0;
         uint32_t w[20];
@@ -1641,7 +1650,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
                 S[4] = fma((double)hi, 65536.0, (double)lo);
             }
             const int64_t i = i0 + u;
-            out[u] = i < m ? crt_finish32<OutT, NP>(S, e[i], fj, cc) : (OutT)0;
+            out[u] = i < m ? crt_finish32<OutT, NP>(S, ei[u], fj, cc) : (OutT)0;
         }
         store_run_nt(C + i0 + j * ldc, out, m - i0);
     }
