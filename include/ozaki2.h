@@ -356,6 +356,25 @@ int ozaki2_cgemm_debug(int64_t m, int64_t n, int64_t k,
  */
 size_t ozaki2_zgemm_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int debug);
 
+/*
+ * Test entry point: the complex reconstruction alone, from given residues of
+ * the three products per modulus ([Q] step 4 for each part: Re = T1 - T2 and
+ * Im = T3 - T1 - T2 in residues, each lifted into (-P/2, P/2], rounded once
+ * and scaled by 2^-(e_i + f_j)), on the kernels ozaki2_zgemm uses.
+ *   residues DEVICE uint8 [3N][n][m]: T_g mod p_l of entry (i, j) at
+ *            residues[((3l + g)*n + j)*m + i], g = 0, 1, 2 for T1, T2, T3,
+ *            each in [0, p_l) (not checked);
+ *   e, f     DEVICE int32 [m], [n] as for ozaki2_crt_debug;
+ *   C, ldc   DEVICE double complex output (interleaved), column-major, ldc in
+ *            complex elements;
+ *   workspace DEVICE, at least ozaki2_zgemm_workspace_size(m, n, 1, N, 0)
+ *            bytes, 256-byte aligned.
+ * Returns as ozaki2_crt_debug.
+ */
+int ozaki2_zcrt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                      const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* Workspace bytes for ozaki2_dgemm_debug (larger: raw int32 products). */
 size_t ozaki2_debug_workspace_size(int64_t m, int64_t n, int64_t k, int num_moduli, int mode);
 

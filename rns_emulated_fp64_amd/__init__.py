@@ -34,7 +34,7 @@ EXPORTS = (
     "ozaki2_finalize", "ozaki2_crt_debug", "ozaki2_sgemm", "ozaki2_sgemm_ws", "ozaki2_sgemm_debug",
     "ozaki2_zgemm", "ozaki2_zgemm_ws", "ozaki2_zgemm_debug", "ozaki2_cgemm", "ozaki2_cgemm_ws", "ozaki2_cgemm_debug",
     "ozaki2_zgemm_workspace_size", "ozaki2_dgemm_noalloc", "ozaki2_dgemm_check", "ozaki2_check_workspace_size",
-    "ozaki2_crt_check_debug",
+    "ozaki2_crt_check_debug", "ozaki2_zcrt_debug",
 )
 
 _lib = None
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.ozaki2_zgemm_workspace_size.restype = sz
     L.ozaki2_crt_debug.argtypes = [i64, i64, i32, p, p, p, p, i64, p, sz, p]
     L.ozaki2_crt_debug.restype = i32
+    L.ozaki2_zcrt_debug.argtypes = L.ozaki2_crt_debug.argtypes
+    L.ozaki2_zcrt_debug.restype = i32
     L.ozaki2_dgemm_check.argtypes = prod + [p, sz, p, p]
     L.ozaki2_dgemm_check.restype = i32
     L.ozaki2_check_workspace_size.argtypes = [i64, i64, i64, i32, i32]
@@ -199,6 +201,10 @@ def ozaki2_zgemm_workspace_size(m, n, k, num_moduli, debug=False) -> int:
 
 def ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream=0) -> int:
     return lib().ozaki2_crt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream)
+
+
+def ozaki2_zcrt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream=0) -> int:
+    return lib().ozaki2_zcrt_debug(m, n, num_moduli, residues, e, f, C, ldc, workspace, workspace_bytes, stream)
 
 
 def ozaki2_max_moduli() -> int:

@@ -417,7 +417,7 @@ int ozaki2_crt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residu
     const Tables *T = get_tables(num_moduli);
     hipStream_t s = (hipStream_t)stream;
     int8_t *planes = (int8_t *)((char *)workspace + L.planes);
-    HIP_TRY(launch_pack_planes(residues, num_moduli, T->mod, m, n, L, planes, s));
+    HIP_TRY(launch_pack_planes(residues, num_moduli, 1, T->mod, m, n, L, planes, s));
     HIP_TRY(launch_crt(Elem::f64, planes, m, n, e, f, T->crt, C, ldc, L, s));
     return OZAKI2_SUCCESS;
 }
@@ -471,7 +471,7 @@ int ozaki2_crt_check_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *
     const Tables *TS = get_tables(num_moduli + 1);
     hipStream_t s = (hipStream_t)stream;
     int8_t *planes = (int8_t *)((char *)workspace + L.planes);
-    HIP_TRY(launch_pack_planes(residues, num_moduli + 1, TS->mod, m, n, L, planes, s));
+    HIP_TRY(launch_pack_planes(residues, num_moduli + 1, 1, TS->mod, m, n, L, planes, s));
     HIP_TRY(launch_crt(Elem::f64, planes, m, n, e, f, T->crt, C, ldc, L, s));
     HIP_TRY(launch_crt_check(planes, m, n, T->check, L, flags_out, s));
     return OZAKI2_SUCCESS;
@@ -527,6 +527,31 @@ size_t ozaki2_zgemm_workspace_size(int64_t m, int64_t n, int64_t k, int num_modu
         return 0;
     if (!layout_fits(m, n, k, OZAKI2_FAST) || m == 0 || n == 0 || k == 0) return 0;
     return make_layout(m, n, k, num_moduli, OZAKI2_FAST, debug != 0, 3).total;
+}
+
+int ozaki2_zcrt_debug(int64_t m, int64_t n, int num_moduli, const uint8_t *residues, const int32_t *e,
+                      const int32_t *f, double *C, int64_t ldc, void *workspace, size_t workspace_bytes,
+                      void *stream) {
+    if (m < 0) return -1;
+    if (n < 0) return -2;
+    if (num_moduli < 2 || num_moduli > kMaxModuli) return -3;
+    const bool any = m > 0 && n > 0;
+    if (residues == nullptr && any) return -4;
+    if (e == nullptr && any) return -5;
+    if (f == nullptr && any) return -6;
+    if (C == nullptr && any) return -7;
+    if (ldc < (m > 1 ? m : 1)) return -8;
+    if (!any) return OZAKI2_SUCCESS;
+    if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0) return -9;
+    if (!layout_fits(m, n, 1, OZAKI2_FAST)) return OZAKI2_ERR_UNSUPPORTED;
+    const Layout L = make_layout(m, n, 1, num_moduli, OZAKI2_FAST, false, 3);
+    if (workspace_bytes < L.total) return OZAKI2_ERR_WORKSPACE;
+    const Tables *T = get_tables(num_moduli);
+    hipStream_t s = (hipStream_t)stream;
+    int8_t *planes = (int8_t *)((char *)workspace + L.planes);
+    HIP_TRY(launch_pack_planes(residues, 3 * num_moduli, 3, T->mod, m, n, L, planes, s));
+    HIP_TRY(launch_crt_complex(Elem::f64, planes, m, n, e, f, T->crt, T->mod, C, ldc, L, s, Ev{}));
+    return OZAKI2_SUCCESS;
 }
 
 int ozaki2_max_moduli(void) { return kMaxModuli; }

@@ -54,6 +54,8 @@ struct CrtConsts {
     int np32;                       // 32-bit pieces for the digit sums and for P (2..5)
     int nd;                         // signed base-256 digits of the weights (<= kMaxDigits)
     int8_t digit[kMaxDigits][32];   // digit[v][l] = v-th digit of W_l, |digit| <= 128; 0 for l >= n
+    int nnd;                        // signed base-256 digits of P - W_l (n <= 16 only; 0 otherwise)
+    int8_t ndigit[16][16];          // ndigit[v][l] = v-th digit of P - W_l (valid when nnd <= 16)
 };
 
 // Constants of the CRT-range check against one redundant modulus pc (the
@@ -148,8 +150,10 @@ hipError_t launch_unpack_residues(const int8_t *packed, int nmod, int64_t rows, 
                                   int64_t rows_pad, const Layout &L, int8_t *out, hipStream_t s);
 hipError_t launch_copy_planes_u8(const int8_t *planes, int nmod, int group, const ModConsts &mc, int64_t m,
                                  int64_t n, const Layout &L, uint8_t *out, hipStream_t s);
-hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
-                              const Layout &L, int8_t *planes, hipStream_t s);
+// residues [nplanes][n][m] in [0, p) -> symmetric int8 planes; plane q is
+// reduced mod p[q / group]
+hipError_t launch_pack_planes(const uint8_t *residues, int nplanes, int group, const ModConsts &mc, int64_t m,
+                              int64_t n, const Layout &L, int8_t *planes, hipStream_t s);
 hipError_t launch_copy_planes_i32(const int32_t *raw, int nmod, int64_t m, int64_t n, const Layout &L,
                                   int32_t *out, hipStream_t s);
 

@@ -1309,7 +1309,10 @@ __device__ __forceinline__ void crt_range_fix(double x[NP], const double P[], co
 // is good to ~2^-37 absolute, so only |S/P - q| within 2^-30 of 1/2 needs the
 // exact wrap check, which valid scalings never reach; the second check catches
 // |X| below ~2^-37 P, where the predicted sign can be wrong.
-template <int BITS, int NP = 4>
+// ZERO_POS: S may be a nonzero multiple of P (the complex form's unreduced
+// residues), so X = 0 can come with either predicted sign; it gets +1, the
+// sign of RN(0) in the oracle.
+template <int BITS, int NP = 4, bool ZERO_POS = false>
 __device__ __forceinline__ void crt_lift(const double S[NP], double x[NP], double &sg, double s_over_base3,
                                          const double P[], const double H[], double pinv_base3) {
     const double quo = s_over_base3 * pinv_base3;
@@ -1333,6 +1336,9 @@ __device__ __forceinline__ void crt_lift(const double S[NP], double x[NP], doubl
         for (int t = 0; t < NP; ++t) x[t] = -x[t];
         normalize4<BITS, NP>(x);
         sg = -sg;
+    }
+    if constexpr (ZERO_POS) {
+        if (sign4<NP>(x) == 0) sg = 1.0;
     }
 }
 
@@ -1431,7 +1437,7 @@ __device__ __forceinline__ OutT crt_finish(const double S[4], int ei, int fj, co
 // As crt_finish for S in NP (2..5) 32-bit pieces, enough for the digit sums
 // and for P (P < 2^(32 NP)). The quotient estimate uses S / 2^(32 (NP - 1))
 // and RN(2^(32 (NP - 1)) / P).
-template <class OutT, int NP = 4>
+template <class OutT, int NP = 4, bool ZERO_POS = false>
 __device__ __forceinline__ OutT crt_finish32(const double S[NP], int ei, int fj, const CrtConsts &cc) {
     double top = S[NP - 1];
     double sc = 1.0;
@@ -1442,7 +1448,7 @@ __device__ __forceinline__ OutT crt_finish32(const double S[NP], int ei, int fj,
     }
     const double pinv = NP == 5 ? cc.pinv128 : NP == 4 ? cc.pinv96 : NP == 3 ? cc.pinv64 : cc.pinv32;
     double x[NP], sg;
-    crt_lift<32, NP>(S, x, sg, top, cc.P32, cc.H32, pinv);
+    crt_lift<32, NP, ZERO_POS>(S, x, sg, top, cc.P32, cc.H32, pinv);
     const double mag = limbs32_to_double<sizeof(OutT) == 4, NP>(x, ei + fj);
     return (ei == kExpNonfinite || fj == kExpNonfinite) ? (OutT)__builtin_nan("") : (OutT)(sg * mag);
 }
@@ -1712,6 +1718,86 @@ __global__ __launch_bounds__(256) void k_crt_c(const int8_t *__restrict__ planes
     }
 }
 
+// Complex products on the matrix cores (up to 16 moduli). By Gauss' trick the
+// real part's weighted sum is sum_l (T1_l - T2_l) W_l and the imaginary part's
+// sum_l (T3_l - T1_l - T2_l) W_l. Both only matter mod P, so a negative weight
+// -W_l can be replaced by P - W_l, and the residues enter unreduced. The digit
+// sums are then int8 products, like those of k_crt_mma: two MFMAs for the real
+// part (T1 against the digits of W, T2 against those of P - W) and three for
+// the imaginary part (T3 against W, T1 and T2 against P - W), accumulated in
+// one 32 x 32 x 32 block each. |D_v| <= 3 * 16 * 128 * 128 < 2^19.6, so the
+// 32-bit pieces stay exact (|piece| < 2^43.6) and |S| <= 2^12 P; the lift
+// and rounding are those of a real entry, except that S can now be a nonzero
+// multiple of P, whose X = 0 must still come out as +0.
+template <class OutT, int NP = 4>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_crt_c_mma(
+    const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
+    const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
+    __shared__ __attribute__((aligned(16))) int8_t digit[2][16][16];
+    if (threadIdx.x < 128) {
+        const int s = threadIdx.x >> 6, v = (threadIdx.x >> 2) & 15, b4 = (threadIdx.x & 3) * 4;
+        *(uint32_t *)&digit[s][v][b4] = s ? *(const uint32_t *)&cc.ndigit[v][b4] : *(const uint32_t *)&cc.digit[v][b4];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 31;
+    const bool mine = ((r >> 2) & 1) == (lane >> 5);
+    const int dv = 4 * (r >> 3) + (r & 3);
+    const v4i aop = mine ? *(const v4i *)&digit[0][dv][0] : (v4i){0, 0, 0, 0};   // digits of W
+    const v4i aopn = mine ? *(const v4i *)&digit[1][dv][0] : (v4i){0, 0, 0, 0};  // digits of P - W
+
+    // four consecutive rows per lane, full wavefronts as in k_crt_mma
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    int ei[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ei[u] = i0 + u < m ? e[i0 + u] : 0;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i0;
+        uint32_t w[3][16];  // w[c][l]: rows i0 .. i0 + 3 of plane 3 l + c
+#pragma unroll
+        for (int l = 0; l < 16; ++l)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                w[c][l] = l < cc.n ? *(const uint32_t *)(src + (int64_t)(3 * l + c) * plane_elems) : 0u;
+        const int fj = f[j];
+        OutT out[8];  // interleaved (re, im) of rows i0 .. i0 + 3
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // B operands of row i0 + u: byte u of the words of each plane group
+            v4i R[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t s01 = __builtin_amdgcn_perm(w[c][4 * g + 1], w[c][4 * g], 0x0c0c0400u + u * 0x0101u);
+                    const uint32_t s23 = __builtin_amdgcn_perm(w[c][4 * g + 3], w[c][4 * g + 2], 0x0c0c0400u + u * 0x0101u);
+                    R[c][g] = (int)__builtin_amdgcn_perm(s23, s01, 0x05040100u);
+                }
+            const int64_t i = i0 + u;
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                v16i D;
+                if (part == 0) {
+                    D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, R[0], (v16i){0}, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aopn, R[1], D, 0, 0, 0);
+                } else {
+                    D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, R[2], (v16i){0}, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aopn, R[0], D, 0, 0, 0);
+                    D = __builtin_amdgcn_mfma_i32_32x32x32_i8(aopn, R[1], D, 0, 0, 0);
+                }
+                double S[NP];
+#pragma unroll
+                for (int t = 0; t < NP; ++t) {
+                    const int lo = D[4 * t] + D[4 * t + 1] * 256, hi = D[4 * t + 2] + D[4 * t + 3] * 256;
+                    S[t] = fma((double)hi, 65536.0, (double)lo);
+                }
+                out[2 * u + part] = i < m ? crt_finish32<OutT, NP, true>(S, ei[u], fj, cc) : (OutT)0;
+            }
+        }
+        store_run_nt(C + 2 * (i0 + j * ldc), out, 2 * (m - i0));
+    }
+}
+
 // CRT-range check against one redundant modulus (debug entry points): the
 // integer X the reconstruction returns from the first ck.n residues must agree
 // with the residue product of the check modulus pc ([Q] section
@@ -1937,11 +2023,11 @@ __global__ void k_copy_planes_red(const int8_t *planes, int64_t m, int64_t m_pad
 
 // [0, p) -> symmetric residues in the padded plane layout (padding zeroed)
 __global__ void k_pack_planes(const uint8_t *res, int64_t m, int64_t n, int64_t m_pad, int64_t plane_elems,
-                              ModConsts mc, int8_t *planes) {
+                              ModConsts mc, int group, int8_t *planes) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t l = blockIdx.z;
     if (i >= m_pad) return;
-    const int p = (int)mc.p[l];
+    const int p = (int)mc.p[l / group];
     for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
         int v = i < m ? res[(l * n + j) * m + i] : 0;
         if (v > (p - 1) / 2) v -= p;
@@ -2228,7 +2314,19 @@ hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t 
                               const int32_t *f, const CrtConsts &cc, const ModConsts &mc, void *C, int64_t ldc,
                               const Layout &L, hipStream_t s, Ev ev) {
     dim3 grid(nblk((m + kCrtRows - 1) / kCrtRows, 256), ydim(n));
-    if (el == Elem::f32) {
+    if (cc.n <= 16 && cc.nd <= 16 && cc.nnd <= 16 && cc.np32 <= 4 &&
+        !(getenv("OZ2_CRT") && strcmp(getenv("OZ2_CRT"), "fma") == 0)) {
+        if (el == Elem::f32) {
+            auto kern = cc.np32 == 2 ? k_crt_c_mma<float, 2> : cc.np32 == 3 ? k_crt_c_mma<float, 3> : k_crt_c_mma<float, 4>;
+            OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, (float *)C,
+                       ldc);
+        } else {
+            auto kern = cc.np32 == 2 ? k_crt_c_mma<double, 2> : cc.np32 == 3 ? k_crt_c_mma<double, 3>
+                                                                              : k_crt_c_mma<double, 4>;
+            OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, (double *)C,
+                       ldc);
+        }
+    } else if (el == Elem::f32) {
         auto kern = k_crt_c<float>;
         OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, mc,
                    (float *)C, ldc);
@@ -2240,10 +2338,11 @@ hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_pack_planes(const uint8_t *residues, int nmod, const ModConsts &mc, int64_t m, int64_t n,
-                              const Layout &L, int8_t *planes, hipStream_t s) {
-    dim3 grid(nblk(L.m_pad, 256), ydim(n), (unsigned)nmod);
-    hipLaunchKernelGGL(k_pack_planes, grid, dim3(256), 0, s, residues, m, n, L.m_pad, L.m_pad * L.n_pad, mc, planes);
+hipError_t launch_pack_planes(const uint8_t *residues, int nplanes, int group, const ModConsts &mc, int64_t m,
+                              int64_t n, const Layout &L, int8_t *planes, hipStream_t s) {
+    dim3 grid(nblk(L.m_pad, 256), ydim(n), (unsigned)nplanes);
+    hipLaunchKernelGGL(k_pack_planes, grid, dim3(256), 0, s, residues, m, n, L.m_pad, L.m_pad * L.n_pad, mc, group,
+                       planes);
     return hipGetLastError();
 }
 

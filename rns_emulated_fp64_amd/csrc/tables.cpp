@@ -175,16 +175,30 @@ void build(Tables &t, int n) {
         U256 W = M.mul_small(K);
         std::memcpy(t.weight[l], W.d, sizeof(W.d));
         chunks40(W, t.crt.w[l]);
-        // signed base-256 digits, least significant first: W = sum_v d_v 256^v
-        U256 rest = W;
-        for (int v = 0; !rest.is_zero(); ++v) {
-            if (v >= kMaxDigits) std::abort();  // cannot happen for P < 2^159
-            uint32_t low = rest.d[0] & 0xffu;
-            int d = low >= 128 ? (int)low - 256 : (int)low;
-            rest = rest.div_small(256, nullptr);
-            if (d < 0) rest = rest.add_small(1);
-            t.crt.digit[v][l] = (int8_t)d;
-            if (v + 1 > t.crt.nd) t.crt.nd = v + 1;
+        // signed base-256 digits, least significant first: X = sum_v d_v 256^v,
+        // d_v in [-128, 127]; returns the digit count
+        auto digits = [](U256 rest, int8_t *out, int stride, int max_digits) {
+            int v = 0;
+            for (; !rest.is_zero(); ++v) {
+                if (v >= max_digits) std::abort();  // cannot happen for P < 2^159
+                uint32_t low = rest.d[0] & 0xffu;
+                int d = low >= 128 ? (int)low - 256 : (int)low;
+                rest = rest.div_small(256, nullptr);
+                if (d < 0) rest = rest.add_small(1);
+                out[v * stride] = (int8_t)d;
+            }
+            return v;
+        };
+        const int nd = digits(W, &t.crt.digit[0][l], 32, kMaxDigits);
+        if (nd > t.crt.nd) t.crt.nd = nd;
+        // P - W_l = M_l (p_l - K_l), congruent to -W_l mod P: its digits stand
+        // in for a negative weight in the complex reconstruction (P < 2^127
+        // there, so 16 digits)
+        if (n <= 16) {
+            int8_t tmp[kMaxDigits] = {};
+            const int nnd = digits(M.mul_small((uint32_t)t.moduli[l] - K), tmp, 1, kMaxDigits);
+            for (int v = 0; v < 16; ++v) t.crt.ndigit[v][l] = tmp[v];
+            if (nnd > t.crt.nnd) t.crt.nnd = nnd;
         }
     }
     chunks40(P, t.crt.P);

@@ -104,6 +104,22 @@ def test_cgemm_ragged(N):
     assert g["C_re"].dtype == np.float32
 
 
+@pytest.mark.parametrize("N", [8, 16])
+@pytest.mark.parametrize("single", [False, True])
+def test_zgemm_exact_zero_parts(N, single):
+    # A = (1 + i) X and B = (1 + i) Y give A B = 2i X Y: the real part is exactly
+    # zero although T1 = T2 is not, and must come out as +0 like RN(0); the
+    # imaginary part of a zero row is zero from zero residues
+    rng = np.random.default_rng(5)
+    X = W.spread_matrix(rng, (70, 90), 1.0)
+    Y = W.spread_matrix(rng, (90, 50), 1.0)
+    X[4, :] = 0.0
+    A, B = (1 + 1j) * X, (1 + 1j) * Y
+    g, r = complex_parity(A, B, N, single)
+    assert np.all(g["C_re"] == 0) and not np.any(np.signbit(g["C_re"]))
+    assert np.all(g["C_im"][4] == 0) and not np.any(np.signbit(g["C_im"][4]))
+
+
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 7, 3), (33, 17, 129), (64, 64, 1)])
 def test_zgemm_tiny_shapes(shape):
     A, B = complex_case(*shape, seed=sum(shape))
