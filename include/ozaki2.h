@@ -51,9 +51,9 @@
  * tiles than compute units, else one tile per block (eight wavefronts);
  * OZ2_GEMM_KERNEL=blocks or =persistent forces either. Results do not depend
  * on any of these settings. OZ2_CRT=fma reconstructs real products
- * with 17 to 20 moduli, and complex products with up to 16, with FP64 FMAs on
- * 40-bit pieces instead of digit sums on the matrix cores (the same results;
- * complex products with more moduli always use the FMA form).
+ * with 17 to 20 moduli, and complex products with any number, with FP64 FMAs
+ * on 40-bit pieces instead of digit sums on the matrix cores (the same
+ * results).
  *
  * Memory ownership: A, B, C and any workspace belong to the caller. The
  * library keeps one cached workspace per device for ozaki2_dgemm (freed by

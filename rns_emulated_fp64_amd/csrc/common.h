@@ -54,8 +54,8 @@ struct CrtConsts {
     int np32;                       // 32-bit pieces for the digit sums and for P (2..5)
     int nd;                         // signed base-256 digits of the weights (<= kMaxDigits)
     int8_t digit[kMaxDigits][32];   // digit[v][l] = v-th digit of W_l, |digit| <= 128; 0 for l >= n
-    int nnd;                        // signed base-256 digits of P - W_l (n <= 16 only; 0 otherwise)
-    int8_t ndigit[16][16];          // ndigit[v][l] = v-th digit of P - W_l (valid when nnd <= 16)
+    int nnd;                        // signed base-256 digits of P - W_l (<= kMaxDigits)
+    int8_t ndigit[kMaxDigits][32];  // ndigit[v][l] = v-th digit of P - W_l; 0 for l >= n
 };
 
 // Constants of the CRT-range check against one redundant modulus pc (the

@@ -1798,6 +1798,104 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     }
 }
 
+// 17..20 moduli: k_crt_c_mma's digit sums in k_crt_mma20's layout. Each plane
+// group gives two B operands (moduli 0..15, and 16..19 in the first four bytes
+// of a second). W and P - W have two digit blocks each: digits 0..15, and
+// digits 16..19 in registers 0..3 of a second result. One term (a plane group
+// against a weight table) is four MFMAs into the part's two blocks: 8 for Re,
+// 12 for Im, per 64 entries. |D_v| <= 3 * 20 * 128 * 128 < 2^20, the five
+// 32-bit pieces stay below 2^44, and |S| <= 2^12.6 P.
+template <class OutT, int NM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_crt_c_mma20(
+    const int8_t *__restrict__ planes, int64_t plane_elems, int64_t m_pad, int64_t m, int64_t n,
+    const int32_t *__restrict__ e, const int32_t *__restrict__ f, CrtConsts cc, OutT *__restrict__ C, int64_t ldc) {
+    constexpr int NP = 5;
+    __shared__ __attribute__((aligned(16))) int8_t digit[2][kMaxDigits][32];
+    for (int t = threadIdx.x; t < 2 * kMaxDigits * 8; t += blockDim.x) {
+        const int sgn = t / (kMaxDigits * 8), v = (t / 8) % kMaxDigits, b4 = (t & 7) * 4;
+        *(uint32_t *)&digit[sgn][v][b4] =
+            sgn ? *(const uint32_t *)&cc.ndigit[v][b4] : *(const uint32_t *)&cc.digit[v][b4];
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 31;
+    const bool mine = ((r >> 2) & 1) == (lane >> 5);
+    const int dv = 4 * (r >> 3) + (r & 3);  // the digit this lane's accumulator row carries
+    const v4i zero = {0, 0, 0, 0};
+    // [0]: digits of W, [1]: digits of P - W
+    v4i a_lo0[2], a_hi0[2], a_lo1[2], a_hi1[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        a_lo0[t] = mine ? *(const v4i *)&digit[t][dv][0] : zero;
+        a_hi0[t] = mine ? (v4i){*(const int *)&digit[t][dv][16], 0, 0, 0} : zero;
+        a_lo1[t] = mine && dv < 4 ? *(const v4i *)&digit[t][16 + (dv & 3)][0] : zero;
+        a_hi1[t] = mine && dv < 4 ? (v4i){*(const int *)&digit[t][16 + (dv & 3)][16], 0, 0, 0} : zero;
+    }
+
+    const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (((int64_t)blockIdx.x * 256 + (threadIdx.x & ~63)) * 4 >= m_pad) return;
+    int ei[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ei[u] = i0 + u < m ? e[i0 + u] : 0;
+    for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+        const int8_t *src = planes + j * m_pad + i0;
+        uint32_t w[3][20];  // w[c][l]: rows i0 .. i0 + 3 of plane 3 l + c
+#pragma unroll
+        for (int l = 0; l < 20; ++l)
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                w[c][l] = l < NM ? *(const uint32_t *)(src + (int64_t)(3 * l + c) * plane_elems) : 0u;
+        const int fj = f[j];
+        OutT out[8];  // interleaved (re, im) of rows i0 .. i0 + 3
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            // B operands of row i0 + u: byte u of the words of each plane group
+            v4i R[3];
+            v4i Bh[3];
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+#pragma unroll
+                for (int g = 0; g < 5; ++g) {
+                    const uint32_t s01 = __builtin_amdgcn_perm(w[c][4 * g + 1], w[c][4 * g], 0x0c0c0400u + u * 0x0101u);
+                    const uint32_t s23 = __builtin_amdgcn_perm(w[c][4 * g + 3], w[c][4 * g + 2], 0x0c0c0400u + u * 0x0101u);
+                    const int q = (int)__builtin_amdgcn_perm(s23, s01, 0x05040100u);
+                    if (g < 4)
+                        R[c][g] = q;
+                    else
+                        Bh[c] = (v4i){q, 0, 0, 0};
+                }
+            }
+            const int64_t i = i0 + u;
+#pragma unroll
+            for (int part = 0; part < 2; ++part) {
+                // (plane group, weight table) terms of this part
+                constexpr int kRe[2][2] = {{0, 0}, {1, 1}};
+                constexpr int kIm[3][2] = {{2, 0}, {0, 1}, {1, 1}};
+                v16i D0 = (v16i){0}, D1 = (v16i){0};
+#pragma unroll
+                for (int t = 0; t < (part == 0 ? 2 : 3); ++t) {
+                    const int c = part == 0 ? kRe[t][0] : kIm[t][0], wt = part == 0 ? kRe[t][1] : kIm[t][1];
+                    D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_lo0[wt], R[c], D0, 0, 0, 0);
+                    D0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_hi0[wt], Bh[c], D0, 0, 0, 0);
+                    D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_lo1[wt], R[c], D1, 0, 0, 0);
+                    D1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_hi1[wt], Bh[c], D1, 0, 0, 0);
+                }
+                double S[NP];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int lo = D0[4 * t] + D0[4 * t + 1] * 256, hi = D0[4 * t + 2] + D0[4 * t + 3] * 256;
+                    S[t] = fma((double)hi, 65536.0, (double)lo);
+                }
+                {
+                    const int lo = D1[0] + D1[1] * 256, hi = D1[2] + D1[3] * 256;
+                    S[4] = fma((double)hi, 65536.0, (double)lo);
+                }
+                out[2 * u + part] = i < m ? crt_finish32<OutT, NP, true>(S, ei[u], fj, cc) : (OutT)0;
+            }
+        }
+        store_run_nt(C + 2 * (i0 + j * ldc), out, 2 * (m - i0));
+    }
+}
+
 // CRT-range check against one redundant modulus (debug entry points): the
 // integer X the reconstruction returns from the first ck.n residues must agree
 // with the residue product of the check modulus pc ([Q] section
@@ -2323,6 +2421,19 @@ hipError_t launch_crt_complex(Elem el, const int8_t *planes, int64_t m, int64_t 
         } else {
             auto kern = cc.np32 == 2 ? k_crt_c_mma<double, 2> : cc.np32 == 3 ? k_crt_c_mma<double, 3>
                                                                               : k_crt_c_mma<double, 4>;
+            OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, (double *)C,
+                       ldc);
+        }
+    } else if (cc.n >= 17 && cc.n <= 20 && cc.nd <= 20 && cc.nnd <= 20 && cc.np32 <= 5 &&
+               !(getenv("OZ2_CRT") && strcmp(getenv("OZ2_CRT"), "fma") == 0)) {
+        if (el == Elem::f32) {
+            auto kern = cc.n == 17 ? k_crt_c_mma20<float, 17> : cc.n == 18 ? k_crt_c_mma20<float, 18>
+                      : cc.n == 19 ? k_crt_c_mma20<float, 19> : k_crt_c_mma20<float, 20>;
+            OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, (float *)C,
+                       ldc);
+        } else {
+            auto kern = cc.n == 17 ? k_crt_c_mma20<double, 17> : cc.n == 18 ? k_crt_c_mma20<double, 18>
+                      : cc.n == 19 ? k_crt_c_mma20<double, 19> : k_crt_c_mma20<double, 20>;
             OZ2_LAUNCH(ev, kern, grid, dim3(256), 0, s, planes, L.m_pad * L.n_pad, L.m_pad, m, n, e, f, cc, (double *)C,
                        ldc);
         }

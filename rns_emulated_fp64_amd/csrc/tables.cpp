@@ -192,14 +192,9 @@ void build(Tables &t, int n) {
         const int nd = digits(W, &t.crt.digit[0][l], 32, kMaxDigits);
         if (nd > t.crt.nd) t.crt.nd = nd;
         // P - W_l = M_l (p_l - K_l), congruent to -W_l mod P: its digits stand
-        // in for a negative weight in the complex reconstruction (P < 2^127
-        // there, so 16 digits)
-        if (n <= 16) {
-            int8_t tmp[kMaxDigits] = {};
-            const int nnd = digits(M.mul_small((uint32_t)t.moduli[l] - K), tmp, 1, kMaxDigits);
-            for (int v = 0; v < 16; ++v) t.crt.ndigit[v][l] = tmp[v];
-            if (nnd > t.crt.nnd) t.crt.nnd = nnd;
-        }
+        // in for a negative weight in the complex reconstruction
+        const int nnd = digits(M.mul_small((uint32_t)t.moduli[l] - K), &t.crt.ndigit[0][l], 32, kMaxDigits);
+        if (nnd > t.crt.nnd) t.crt.nnd = nnd;
     }
     chunks40(P, t.crt.P);
     U256 H = P.div_small(2, nullptr);

@@ -8,7 +8,7 @@ residues). Targets Xr, Xi are picked on the edges of (-P/2, P/2] ([Q] section
 of the symmetric range so that T1 - T2 and T3 - T1 - T2 reach their largest
 magnitudes), then T2 = T1 - Xr and T3 = Xi + T1 + T2 mod p. Both parts of C
 must equal the oracle's RN(X) * 2^-(e_i + f_j) bit for bit, on the matrix-core
-form (up to 16 moduli) and on the FP64-FMA form (more moduli, or OZ2_CRT=fma).
+forms (the default for 2..20 moduli) and on the FP64-FMA form (OZ2_CRT=fma).
 """
 from __future__ import annotations
 
@@ -97,15 +97,15 @@ def _zcrt(N: int, extreme: bool):
     assert max(Xr.max(), Xi.max()) == P // 2 and min(Xr.min(), Xi.min()) == -(P // 2) + 1
 
 
-# 2..7 moduli: two 32-bit pieces, 8..12: three, 13..16: four (matrix cores);
-# 17..20: the FP64-FMA form
-@pytest.mark.parametrize("N", [2, 5, 8, 12, 13, 16, 17, 20])
+# 2..7 moduli: two 32-bit pieces, 8..12: three, 13..16: four; 17..20: five
+# (two digit blocks per part); all on the matrix cores by default
+@pytest.mark.parametrize("N", [2, 5, 8, 12, 13, 16, 17, 18, 19, 20])
 @pytest.mark.parametrize("extreme", [False, True])
 def test_zcrt_edges_bitwise(N, extreme):
     _zcrt(N, extreme)
 
 
-@pytest.mark.parametrize("N", [3, 9, 16])
+@pytest.mark.parametrize("N", [3, 9, 16, 18, 20])
 def test_zcrt_edges_bitwise_fma_form(monkeypatch, N):
     monkeypatch.setenv("OZ2_CRT", "fma")
     _zcrt(N, True)
