@@ -96,3 +96,27 @@ def test_persistent_complex(monkeypatch):
     assert np.array_equal(g1["red"], g0["red"]), "reduced planes differ"
     assert_bitwise_equal(g1["C_re"], g0["C_re"], "Re C")
     assert_bitwise_equal(g1["C_im"], g0["C_im"], "Im C")
+
+
+def _walking_cases(seed=7201, count=8):
+    # more 256 x 256 tiles than compute units (5 x 5 x 11 = 275 at the least),
+    # ragged edges, padded leading dimensions, both modes
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        m, n = (int(x) for x in rng.integers(1030, 1301, size=2))
+        k = int(rng.integers(250, 1100))
+        N = int(rng.integers(11, 21))
+        mode = "accurate" if rng.random() < 0.3 else "fast"
+        pads = [int(x) for x in rng.integers(0, 4, size=3)]
+        out.append((m, n, k, N, mode, pads, int(rng.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("m,n,k,N,mode,pads,seed", _walking_cases(),
+                         ids=lambda v: None if not isinstance(v, tuple) else str(v))
+def test_persistent_random_shapes_against_oracle(m, n, k, N, mode, pads, seed):
+    assert -(-m // 256) * -(-n // 256) * N > 256  # the persistent kernel by default
+    A, B = W.spread_case(m, n, k, 1.0, seed=seed)
+    full_parity(A, B, N, mode, lda=m + pads[0], ldb=k + pads[1], ldc=m + pads[2], want_prod=False)
+
