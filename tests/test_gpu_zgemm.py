@@ -97,7 +97,7 @@ def test_zgemm_ragged(N):
     complex_parity(A, B, N)
 
 
-@pytest.mark.parametrize("N", [6, 8, 16])
+@pytest.mark.parametrize("N", [6, 8, 16, 18])
 def test_cgemm_ragged(N):
     A, B = complex_case(270, 260, 200, seed=500 + N)
     g, r = complex_parity(A.astype(np.complex64), B.astype(np.complex64), N, single=True)
